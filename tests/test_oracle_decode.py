@@ -1,0 +1,108 @@
+"""Pins of the oracle's batched decode step (CPU only)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, decode, sharding
+
+SCALE = 1.0 / np.sqrt(192.0)
+
+
+def _make(rng, B, Tq, H, lens):
+    q = rng.standard_normal((B, Tq, H, 576))
+    store = [rng.standard_normal((int(L), 576)) for L in lens]
+
+    def rows(b, pos):
+        r = store[b][np.asarray(pos, dtype=np.int64)]
+        return r[:, :512], r[:, 512:]
+    return q, store, rows
+
+
+def _sdpa(q, k, scale):
+    qt = torch.from_numpy(q)[None, :, None, :]
+    kt = torch.from_numpy(k)[None, None].expand(1, q.shape[0], -1, -1)
+    vt = torch.from_numpy(np.ascontiguousarray(k[:, :512]))[None, None].expand(1, q.shape[0], -1, -1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[0, :, 0].numpy()
+
+
+def test_dense_single_token_sees_whole_context():
+    rng = np.random.default_rng(1)
+    lens = [1, 5, 64, 130]
+    q, store, rows = _make(rng, 4, 1, 3, lens)
+    r = decode.mla_decode(q, rows, np.array(lens), 1, 3, SCALE)
+    for b in range(4):
+        assert np.allclose(r["o"][b, 0], _sdpa(q[b, 0], store[b], SCALE), atol=1e-12)
+
+
+def test_causal_range_of_two_query_tokens():
+    # the last cached row is the second query token's own KV: query 0 must
+    # not see it, query 1 must.
+    rng = np.random.default_rng(2)
+    L = 40
+    q, store, rows = _make(rng, 1, 2, 2, [L])
+    big = q[0, 1, 0] * (80.0 / SCALE / (q[0, 1, 0] @ q[0, 1, 0]))
+    store[0][L - 1] = big
+    r = decode.mla_decode(q, rows, np.array([L]), 2, 1, SCALE)
+    assert np.allclose(r["o"][0, 1, 0], big[:512], atol=1e-9)
+    assert np.allclose(r["o"][0, 0], _sdpa(q[0, 0], store[0][:L - 1], SCALE), atol=1e-12)
+    assert np.allclose(r["o"][0, 1], _sdpa(q[0, 1], store[0][:L], SCALE), atol=1e-12)
+
+
+def test_per_shard_partial_is_attention_over_owned_tokens():
+    rng = np.random.default_rng(3)
+    lens = [70, 9]
+    N = 4
+    q, store, rows = _make(rng, 2, 1, 2, lens)
+    r = decode.mla_decode(q, rows, np.array(lens), 1, N, SCALE)
+    for b, L in enumerate(lens):
+        for s in range(N):
+            owned = [p for p in range(L) if p % N == s]   # dealt one at a time
+            o, l = attention.attend(q[b, 0], store[b][owned], store[b][owned][:, :512], SCALE)
+            assert np.allclose(r["o_shards"][s, b, 0], o, atol=1e-13)
+            assert np.allclose(r["lse_shards"][s, b, 0], l, atol=1e-13)
+        om, lm = attention.merge(r["o_shards"][:, b], r["lse_shards"][:, b])
+        assert np.allclose(om, r["o"][b], atol=1e-12) and np.allclose(lm, r["lse"][b], atol=1e-12)
+
+
+def test_more_shards_than_tokens_gives_identity_rows():
+    rng = np.random.default_rng(4)
+    q, store, rows = _make(rng, 1, 1, 2, [3])
+    r = decode.mla_decode(q, rows, np.array([3]), 1, 8, SCALE)
+    for s in range(3, 8):
+        assert np.all(r["o_shards"][s] == 0) and np.all(np.isneginf(r["lse_shards"][s]))
+    assert np.allclose(r["o"][0, 0], _sdpa(q[0, 0], store[0], SCALE), atol=1e-12)
+
+
+def test_sparse_uses_only_selected_rows():
+    rng = np.random.default_rng(5)
+    L, K, N = 500, 33, 8
+    q, store, rows = _make(rng, 1, 2, 4, [L])
+    idx = np.full((1, 2, K + 3), -1, dtype=np.int32)
+    for j in range(2):
+        idx[0, j, :K] = rng.choice(L - 2 + j + 1, size=K, replace=False)
+    r = decode.mla_decode(q, rows, np.array([L]), 2, N, SCALE, topk_idx=idx)
+    for j in range(2):
+        sel = idx[0, j][idx[0, j] >= 0]
+        assert np.allclose(r["o"][0, j], _sdpa(q[0, j], store[0][sel], SCALE), atol=1e-12)
+        for s in range(N):
+            loc = sharding.localize(idx[0, j], s, N)
+            mine = sharding.global_position(loc[loc >= 0], s, N)
+            o, l = attention.attend(q[0, j], store[0][mine], store[0][mine][:, :512], SCALE)
+            assert np.allclose(r["o_shards"][s, 0, j], o, atol=1e-13)
+
+
+def test_sparse_rejects_index_beyond_prefix():
+    rng = np.random.default_rng(6)
+    q, store, rows = _make(rng, 1, 2, 1, [10])
+    idx = np.array([[[9, 0], [3, 1]]], dtype=np.int32)  # query 0 may see 0..8
+    with pytest.raises(ValueError):
+        decode.mla_decode(q, rows, np.array([10]), 2, 2, SCALE, topk_idx=idx)
+
+
+def test_sparse_row_with_no_valid_index():
+    rng = np.random.default_rng(7)
+    q, store, rows = _make(rng, 1, 1, 2, [10])
+    idx = np.full((1, 1, 4), -1, dtype=np.int32)
+    r = decode.mla_decode(q, rows, np.array([10]), 1, 2, SCALE, topk_idx=idx)
+    assert np.all(r["o"] == 0) and np.all(np.isneginf(r["lse"]))
+    assert np.all(r["o_shards"] == 0) and np.all(np.isneginf(r["lse_shards"]))
