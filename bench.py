@@ -1,0 +1,206 @@
+"""Throughput of one sequence-sharded MLA decode step on one MI355X.
+
+A step is the whole hot path over one batch: the partial decode of every
+emulated shard (one launch over all shards) followed by the LSE merge of the
+shard partials.  Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line.  `value` is the achieved HBM bandwidth of the step in
+GB/s, counting algorithmic bytes only (every attended cache row once, the
+query once, each shard partial written once and read once, the final output
+once); `kv_tokens_per_s` and `pct_of_peak` ride along.  The `roofline` object
+reports the dominant kernel (the partial decode launch) timed with HIP events
+on the stream it runs on; `cpu_baseline` times the float64 oracle on a bounded
+sample of the same workload on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "dense_bf16_32k"
+METRIC = "MLA decode attention: achieved HBM GB/s (% of peak) and KV tokens/s at 32K"
+KERNEL_SOURCES = ["decode_valu.hpp", "decode_mfma.hpp", "common.hpp", "params.hpp", "api.hip",
+                  "reduce.hpp", "plan.hpp", "host.cpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "sequence_sharded_mla_amd", "csrc", name)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(x, out_bytes=2, q_bytes=2):
+    """(step bytes, decode-launch bytes, attended KV tokens)."""
+    from sequence_sharded_mla_amd.layout import ROW_BYTES
+    sp = x.spec
+    B, Tq, H, N = sp.batch, sp.q_len, sp.heads, sp.n_shards
+    if x.topk_idx is None:
+        tokens = int(sum(max(int(L) - Tq + j + 1, 0) for L in x.context_lens for j in range(Tq)))
+        idx_bytes = 0
+    else:
+        tokens = int((x.topk_idx >= 0).sum())
+        idx_bytes = x.topk_idx.size * 4
+    kv = tokens * ROW_BYTES[sp.kv_dtype]
+    q = B * Tq * H * 576 * q_bytes
+    part = N * B * Tq * H * (512 * out_bytes + 4)
+    final = B * Tq * H * (512 * out_bytes + 4)
+    decode_launch = kv + q + idx_bytes + part
+    step = decode_launch + part + final
+    return step, decode_launch, tokens
+
+
+def cpu_baseline(x, budget_s=10.0):
+    """Time the float64 oracle (shard partials + merge) on whole requests."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention, decode as odecode
+    sp = x.spec
+    q = odecode.query_to_f64(x.q, sp.q_dtype)
+    rows = odecode.storage_rows(sp.kv_dtype, x.latent, x.scales, x.rope, x.row_offsets, x.row_pos)
+    done, tokens, t0 = 0, 0, time.perf_counter()
+    while done < sp.batch and (time.perf_counter() - t0) < budget_s:
+        b = done
+        r = odecode.mla_decode(q, rows, x.context_lens, sp.q_len, sp.n_shards, sp.scale,
+                               topk_idx=x.topk_idx, requests=[b], full=False)
+        attention.merge(r["o_shards"], r["lse_shards"])
+        if x.topk_idx is None:
+            tokens += sum(max(int(x.context_lens[b]) - sp.q_len + j + 1, 0) for j in range(sp.q_len))
+        else:
+            tokens += int((x.topk_idx[b] >= 0).sum())
+        done += 1
+    dt = time.perf_counter() - t0
+    from sequence_sharded_mla_amd.layout import ROW_BYTES
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    kv_bytes = tokens * ROW_BYTES[sp.kv_dtype]
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s",
+            "kv_tokens_per_s": round(tokens / dt, 1), "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {sp.batch} requests (all {sp.n_shards} shards + merge), "
+                      f"{tokens} attended tokens, {dt:.1f} s"}
+
+
+def traffic_for(workload, khash):
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("kernel_hash") != khash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sharded step is emulated on a single device)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workload
+    from sequence_sharded_mla_amd import layout, mla_get_device_error
+    from sequence_sharded_mla_amd.step import ShardedDecodeStep
+
+    sp = workload.SPECS[args.workload]
+    log(f"bench: generating {sp.name}")
+    t0 = time.perf_counter()
+    x = workload.generate(sp)
+    log(f"bench: generated {x.total_rows} rows in {time.perf_counter() - t0:.1f} s; packing")
+    cache = layout.pack(x, device="cuda")
+    step = ShardedDecodeStep(cache, sp.out_dtype)
+    stream = torch.cuda.current_stream()
+    out_b = 2 if sp.out_dtype == "bf16" else 4
+    q_b = 2 if sp.q_dtype == "bf16" else 4
+    step_bytes, launch_bytes, tokens = algorithmic_bytes(x, out_b, q_b)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert mla_get_device_error(step.workspace) == 0
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    log(f"bench: timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        a, b, c = ev[i]
+        a.record(stream)
+        step.partials()
+        b.record(stream)
+        step.merge()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    t_part = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    t_merge = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    assert mla_get_device_error(step.workspace) == 0
+
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    part_ms = float(np.mean(t_part))
+    achieved = launch_bytes / (part_ms * 1e-3) / 1e9
+    khash = kernel_hash()
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sp.q_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) query/latent/rope, random-permuted paged blocks)",
+        "config": {"workload": sp.name, "batch": sp.batch, "q_len": sp.q_len, "heads": sp.heads,
+                   "context": sp.context or list(sp.ctx_range), "n_shards": sp.n_shards,
+                   "kv_cache": sp.kv_dtype, "topk": sp.topk, "block_size": 64},
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "kernels_ms": {"decode_partials": round(part_ms, 4),
+                       "decode_partials_p10_p90": [round(float(np.percentile(t_part, 10)), 4),
+                                                   round(float(np.percentile(t_part, 90)), 4)],
+                       "lse_merge": round(float(np.mean(t_merge)), 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for(sp.name, khash),
+                     "kernel": "decode partials (all shards, one launch)",
+                     "algorithmic_bytes_per_launch": int(launch_bytes)},
+        "kernel_hash": khash,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host")
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * mla_dcp.h -- C ABI of the sequence-sharded MLA decode library (gfx950).
+ *
+ * One decode step of multi-head latent attention (MLA): H query heads share
+ * one latent KV head whose per-token row holds 512 latent and 64 rope
+ * dimensions ("GLM-5.2 vLLM Decode Context Parallelism", section "Understand
+ * the cache-copy opportunity"; "The Final Verification: Confirming a 200k
+ * Context Deployment on GLM-5", section "The Decision-Making Process Visible
+ * in the Reasoning").  The cache is sharded along the sequence: global token
+ * p of a request lives on shard p mod N as that shard's local token p div N
+ * ("How vLLM Serves GLM-5.3 with Million-Token Contexts on 16 H200s", section
+ * "The core design").  Each shard returns a partial output and the softmax
+ * log-sum-exp of its tokens; the LSE merge combines the partials into the
+ * full-context result ("GLM-5.2 vLLM Decode Context Parallelism", section
+ * "See why vLLM 0.26.0 fails").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor arguments are DEVICE pointers unless stated otherwise.  The caller
+ *   owns all memory; the library keeps no pointer after a call returns and
+ *   allocates no device memory inside the decode, merge and localise calls.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *   is enqueued asynchronously on it; inputs must stay valid and outputs
+ *   untouched until it completes.
+ * - Every call validates its arguments on the host and returns a status
+ *   before anything is enqueued.  On a non-zero status nothing is enqueued
+ *   and no output is written.
+ * - Inputs and outputs must not alias.  Pointers to q, the KV pool and all
+ *   outputs must be 16-byte aligned (MLA_ERR_ALIGN otherwise).
+ * - Empty rows are never undefined: a (request, query token) with no token to
+ *   attend on a shard yields output 0 and LSE -inf ("GLM-5.2 vLLM Decode
+ *   Context Parallelism", section "Separate the backend merge from stable").
+ *
+ * Layouts (row-major, innermost last)
+ * -----------------------------------
+ *   q            [B][Tq][H][576]        q_dtype; 512 latent then 64 rope dims
+ *   kv_pool      [pool_blocks][64][row] one row per token:
+ *                  MLA_F32    576 x f32                          (2304 B)
+ *                  MLA_BF16   576 x bf16                         (1152 B)
+ *                  MLA_FP8_DS 512 x E4M3FN code, 4 x f32 scale (one per
+ *                             128-dim group), 64 x bf16 rope     ( 656 B)
+ *                  latent value d = decode(code[d]) * scale[d / 128]
+ *   block_table  [B][max_blocks] int32, ONE shard's table: local token j of
+ *                request b is row (j % 64) of pool block block_table[b][j/64]
+ *   context_lens [B] int32: tokens in request b's whole (unsharded) cache,
+ *                including the Tq query tokens' own rows; query token t
+ *                (0 <= t < Tq) sits at global position L_b - Tq + t and
+ *                attends positions 0 .. L_b - Tq + t
+ *   topk_idx     [B][Tq][topk] int32 GLOBAL positions (negative = unused);
+ *                a shard attends only the entries it owns (sparse mode)
+ *   o_partial    [B*Tq][H][512] out_dtype     (token/head form)
+ *   lse          [B*Tq][H] f32, natural log of sum exp(scale * q.k)
+ *
+ * Device-detected errors
+ * ----------------------
+ * A block-table row too narrow for a request's local length, a block id
+ * outside [0, pool_blocks), or a top-K index outside the query token's causal
+ * prefix sets a bit in the first 32-bit word of the workspace; the offending
+ * tokens are skipped (treated as not attended).  The word is sticky: it is
+ * cleared only by mla_clear_device_error, and read by mla_get_device_error.
+ */
+#ifndef MLA_DCP_H
+#define MLA_DCP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_NULL 1        /* a required pointer is NULL                    */
+#define MLA_ERR_SHAPE 2       /* a size is out of range or inconsistent        */
+#define MLA_ERR_SHARD 3       /* shard id / shard range / shard count invalid  */
+#define MLA_ERR_UNSUPPORTED 4 /* head count, dimension or dtype not built      */
+#define MLA_ERR_WORKSPACE 5   /* workspace smaller than the size query         */
+#define MLA_ERR_DEVICE 6      /* a HIP runtime call failed                     */
+#define MLA_ERR_ALIGN 7       /* a pointer is not 16-byte aligned              */
+
+/* Element / row formats. */
+#define MLA_F32 0
+#define MLA_BF16 1
+#define MLA_FP8_DS 2
+
+/* Bits of the device error word. */
+#define MLA_DEVERR_BLOCK_TABLE 1u /* table too narrow, or block id out of pool */
+#define MLA_DEVERR_INDEX 2u       /* top-K index beyond the causal prefix      */
+
+/* Shape of one decode step.  Fixed by this build: kv_lora_rank = 512,
+ * rope_dim = 64, block_size = 64; num_heads in {16, 32, 64, 128} (the query
+ * head envelope, "GLM-5.2 vLLM Decode Context Parallelism", section
+ * "Calculate the GLM-5.2 head envelope": heads are padded to a supported
+ * envelope and anything else is refused, not run). */
+typedef struct mla_decode_desc {
+    int32_t batch;        /* B >= 0 (0 = nothing to do)                    */
+    int32_t q_len;        /* Tq >= 1 query tokens per request               */
+    int32_t num_heads;    /* H                                              */
+    int32_t kv_lora_rank; /* must be 512                                    */
+    int32_t rope_dim;     /* must be 64                                     */
+    int32_t block_size;   /* must be 64                                     */
+    int32_t max_blocks;   /* width of each block-table row, >= 1            */
+    int32_t topk;         /* 0 = dense; else entries per query token (<= 65536) */
+    int32_t q_dtype;      /* MLA_F32 (with MLA_F32 cache) or MLA_BF16       */
+    int32_t kv_dtype;     /* MLA_F32, MLA_BF16 or MLA_FP8_DS                */
+    int32_t out_dtype;    /* MLA_F32 or MLA_BF16                            */
+    float softmax_scale;  /* finite; scores are scale * q.k                 */
+    int64_t pool_blocks;  /* number of blocks in kv_pool, >= 1              */
+} mla_decode_desc;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mla_status_string(int32_t status);
+
+/* Tokens of a context of length context_len that shard shard_id of n_shards
+ * stores under round-robin ownership: ceil((L - s) / N) for s < L, else 0.
+ * Returns -1 for invalid arguments (n_shards < 1, shard outside [0, N),
+ * negative length).  Host function. */
+int32_t mla_shard_local_len(int32_t context_len, int32_t shard_id, int32_t n_shards);
+
+/* Bytes of one cache row for a kv dtype (2304, 1152, 656), or -1. */
+int64_t mla_kv_row_bytes(int32_t kv_dtype);
+
+/* Workspace bytes that mla_decode_partial (shard_count = 1) or
+ * mla_decode_partial_shards (shard_count shards) needs for `desc`.  Pure host
+ * function: validates desc (same checks and codes as the decode calls) and
+ * writes the size to *bytes_out.  The size is at least 256 (the device error
+ * word lives in the first 4 bytes). */
+int32_t mla_decode_workspace_size(const mla_decode_desc* desc, int32_t shard_count,
+                                  int64_t* bytes_out);
+
+/* Partial decode attention of ONE shard (the call one DCP rank makes).
+ * Computes, for every request b, query token t and head h, attention over the
+ * tokens shard `shard_id` of `n_shards` owns (dense: all owned positions in
+ * the causal prefix; sparse: owned entries of topk_idx[b][t]), writing the
+ * normalised partial output and its LSE ("GLM-5.2 vLLM Decode Context
+ * Parallelism", sections "See why vLLM 0.26.0 fails" and "Separate the backend
+ * merge from stable").  topk_idx must be NULL when desc->topk == 0 and
+ * non-NULL otherwise.  workspace: device memory of workspace_bytes >=
+ * mla_decode_workspace_size(desc, 1); its first word is the sticky device
+ * error word, the rest is scratch overwritten by the call. */
+int32_t mla_decode_partial(const mla_decode_desc* desc, const void* q, const void* kv_pool,
+                           const int32_t* block_table, const int32_t* context_lens,
+                           const int32_t* topk_idx, int32_t shard_id, int32_t n_shards,
+                           void* o_partial, float* lse, void* workspace,
+                           int64_t workspace_bytes, void* stream);
+
+/* The same for shards shard_begin .. shard_begin + shard_count - 1 of
+ * n_shards in one launch (all shards of one cache emulated on one GPU).
+ *   block_tables [shard_count][B][max_blocks]
+ *   o_partials   [shard_count][B*Tq][H][512] out_dtype
+ *   lses         [shard_count][B*Tq][H] f32
+ * workspace_bytes >= mla_decode_workspace_size(desc, shard_count). */
+int32_t mla_decode_partial_shards(const mla_decode_desc* desc, const void* q,
+                                  const void* kv_pool, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* topk_idx,
+                                  int32_t shard_begin, int32_t shard_count, int32_t n_shards,
+                                  void* o_partials, float* lses, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
+
+/* LSE merge of n_parts partials ("GLM-5.2 vLLM Decode Context Parallelism",
+ * sections "See why vLLM 0.26.0 fails" and "Frequently asked questions"):
+ *   M = max_s lse[s]; w_s = exp(lse[s] - M);
+ *   o_out = sum_s w_s o[s] / sum_s w_s;  lse_out = M + log(sum_s w_s);
+ * rows whose parts all have LSE -inf give (0, -inf) (the neutral row of an
+ * empty shard drops out).  A part with LSE -inf contributes nothing, whatever
+ * its o values.
+ *   o_parts   [n_parts][rows][dv] part_dtype (MLA_F32 or MLA_BF16)
+ *   lse_parts [n_parts][rows] f32
+ *   o_out     [rows][dv] out_dtype;  lse_out [rows] f32, or NULL
+ * 1 <= n_parts <= 64, rows >= 0, dv in {512}. */
+int32_t mla_lse_merge(int32_t n_parts, int64_t rows, int32_t dv, int32_t part_dtype,
+                      const void* o_parts, const float* lse_parts, int32_t out_dtype,
+                      void* o_out, float* lse_out, void* stream);
+
+/* Localise global top-K indices to one shard ("GLM-5.2 vLLM Decode Context
+ * Parallelism", section "Separate the backend merge from stable"):
+ *   local_idx[i] = global_idx[i] div n_shards  if global_idx[i] >= 0 and
+ *                                                global_idx[i] mod n_shards == shard_id
+ *                = -1                           otherwise.
+ * count >= 0 int32 entries; bit-exact. */
+int32_t mla_localize_indices(const int32_t* global_idx, int64_t count, int32_t shard_id,
+                             int32_t n_shards, int32_t* local_idx, void* stream);
+
+/* Read the device error word of a workspace: waits for `stream`, then copies
+ * the word to *code_out (0 = no error; else MLA_DEVERR_* bits). */
+int32_t mla_get_device_error(const void* workspace, int32_t* code_out, void* stream);
+
+/* Enqueue a reset of the device error word to 0 on `stream`. */
+int32_t mla_clear_device_error(void* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DCP_H */

@@ -1,0 +1,179 @@
+// extern "C" entry points of libmla_dcp: argument checks, plan, launches.
+#include <hip/hip_runtime.h>
+
+#include "../../include/mla_dcp.h"
+#include "common.hpp"
+#include "decode_valu.hpp"
+#include "params.hpp"
+#include "plan.hpp"
+#include "reduce.hpp"
+
+namespace mla {
+namespace {
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int32_t launch_status() {
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_DEVICE;
+}
+
+int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* topk_idx, int32_t shard_begin, int32_t shard_count,
+                    int32_t n_shards, void* o, float* lse, void* ws, int64_t ws_bytes,
+                    void* stream) {
+    Plan plan;
+    int32_t st = make_plan(d, shard_count, &plan);
+    if (st != MLA_OK) return st;
+    if (n_shards < 1 || shard_begin < 0 || shard_begin + shard_count > n_shards)
+        return MLA_ERR_SHARD;
+    if (!q || !kv_pool || !block_tables || !context_lens || !o || !lse || !ws) return MLA_ERR_NULL;
+    if (d->topk > 0 && !topk_idx) return MLA_ERR_NULL;
+    if (d->topk == 0 && topk_idx) return MLA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(o) || !aligned16(ws) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return MLA_ERR_ALIGN;
+    if (ws_bytes < plan.ws_bytes) return MLA_ERR_WORKSPACE;
+    if (d->batch == 0) return MLA_OK;
+
+    DecodeParams p{};
+    p.q = q;
+    p.kv = static_cast<const uint8_t*>(kv_pool);
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.topk_idx = topk_idx;
+    p.o_out = o;
+    p.lse_out = lse;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    p.err = reinterpret_cast<uint32_t*>(w);
+    if (plan.n_chunks > 1) {
+        p.ws_o = reinterpret_cast<float*>(w + plan.ws_o_off);
+        p.ws_lse = reinterpret_cast<float*>(w + plan.ws_lse_off);
+        p.ws_cnt = reinterpret_cast<uint32_t*>(w + plan.ws_cnt_off);
+    }
+    p.pool_blocks = d->pool_blocks;
+    p.row_bytes = int32_t(row_bytes(d->kv_dtype));
+    p.B = d->batch;
+    p.Tq = d->q_len;
+    p.H = d->num_heads;
+    p.max_blocks = d->max_blocks;
+    p.topk = d->topk;
+    p.shard_begin = shard_begin;
+    p.shard_count = shard_count;
+    p.n_shards = n_shards;
+    p.n_chunks = plan.n_chunks;
+    p.tiles_per_chunk = plan.tiles_per_chunk;
+    p.out_dtype = d->out_dtype;
+    p.scale = d->softmax_scale;
+
+    hipStream_t s = as_stream(stream);
+    const dim3 grid(uint32_t(plan.rows) * plan.n_chunks, uint32_t(d->num_heads / valu::kHeads));
+    switch (d->kv_dtype) {
+        case MLA_F32:
+            hipLaunchKernelGGL(valu::decode_valu_kernel<MLA_F32>, grid, dim3(valu::kThreads), 0, s, p);
+            break;
+        case MLA_BF16:
+            hipLaunchKernelGGL(valu::decode_valu_kernel<MLA_BF16>, grid, dim3(valu::kThreads), 0, s, p);
+            break;
+        default:
+            hipLaunchKernelGGL(valu::decode_valu_kernel<MLA_FP8_DS>, grid, dim3(valu::kThreads), 0, s, p);
+            break;
+    }
+    if ((st = launch_status()) != MLA_OK) return st;
+    if (plan.n_chunks > 1) {
+        hipLaunchKernelGGL(chunk_combine_kernel, dim3(uint32_t(plan.rows), uint32_t(d->num_heads / 2)),
+                           dim3(256), 0, s, p);
+        if ((st = launch_status()) != MLA_OK) return st;
+    }
+    return MLA_OK;
+}
+
+}  // namespace
+}  // namespace mla
+
+extern "C" {
+
+int32_t mla_decode_partial(const mla_decode_desc* desc, const void* q, const void* kv_pool,
+                           const int32_t* block_table, const int32_t* context_lens,
+                           const int32_t* topk_idx, int32_t shard_id, int32_t n_shards,
+                           void* o_partial, float* lse, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+    if (n_shards < 1 || shard_id < 0 || shard_id >= n_shards) {
+        if (!desc) return MLA_ERR_NULL;
+        int32_t st = mla::validate_desc(desc);
+        return st != MLA_OK ? st : MLA_ERR_SHARD;
+    }
+    return mla::decode_impl(desc, q, kv_pool, block_table, context_lens, topk_idx, shard_id, 1,
+                            n_shards, o_partial, lse, workspace, workspace_bytes, stream);
+}
+
+int32_t mla_decode_partial_shards(const mla_decode_desc* desc, const void* q,
+                                  const void* kv_pool, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* topk_idx,
+                                  int32_t shard_begin, int32_t shard_count, int32_t n_shards,
+                                  void* o_partials, float* lses, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+    return mla::decode_impl(desc, q, kv_pool, block_tables, context_lens, topk_idx, shard_begin,
+                            shard_count, n_shards, o_partials, lses, workspace, workspace_bytes,
+                            stream);
+}
+
+int32_t mla_lse_merge(int32_t n_parts, int64_t rows, int32_t dv, int32_t part_dtype,
+                      const void* o_parts, const float* lse_parts, int32_t out_dtype,
+                      void* o_out, float* lse_out, void* stream) {
+    if (n_parts < 1 || n_parts > 64 || rows < 0) return MLA_ERR_SHAPE;
+    if (dv != mla::kLatent) return MLA_ERR_UNSUPPORTED;
+    if ((part_dtype != MLA_F32 && part_dtype != MLA_BF16) ||
+        (out_dtype != MLA_F32 && out_dtype != MLA_BF16))
+        return MLA_ERR_UNSUPPORTED;
+    if (!o_parts || !lse_parts || !o_out) return MLA_ERR_NULL;
+    if (!mla::aligned16(o_parts) || !mla::aligned16(o_out) ||
+        (reinterpret_cast<uintptr_t>(lse_parts) & 3u) ||
+        (reinterpret_cast<uintptr_t>(lse_out) & 3u))
+        return MLA_ERR_ALIGN;
+    if (rows == 0) return MLA_OK;
+    if (rows > (int64_t(1) << 31)) return MLA_ERR_SHAPE;
+    const dim3 grid(uint32_t((rows + 1) / 2));
+    hipStream_t s = mla::as_stream(stream);
+    if (part_dtype == MLA_F32)
+        hipLaunchKernelGGL(mla::lse_merge_kernel<float>, grid, dim3(256), 0, s, n_parts, rows,
+                           static_cast<const float*>(o_parts), lse_parts, out_dtype, o_out, lse_out);
+    else
+        hipLaunchKernelGGL(mla::lse_merge_kernel<uint16_t>, grid, dim3(256), 0, s, n_parts, rows,
+                           static_cast<const uint16_t*>(o_parts), lse_parts, out_dtype, o_out,
+                           lse_out);
+    return mla::launch_status();
+}
+
+int32_t mla_localize_indices(const int32_t* global_idx, int64_t count, int32_t shard_id,
+                             int32_t n_shards, int32_t* local_idx, void* stream) {
+    if (count < 0) return MLA_ERR_SHAPE;
+    if (n_shards < 1 || shard_id < 0 || shard_id >= n_shards) return MLA_ERR_SHARD;
+    if (count == 0) return MLA_OK;
+    if (!global_idx || !local_idx) return MLA_ERR_NULL;
+    int64_t blocks = (count + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(mla::localize_kernel, dim3(uint32_t(blocks)), dim3(256), 0,
+                       mla::as_stream(stream), global_idx, count, shard_id, n_shards, local_idx);
+    return mla::launch_status();
+}
+
+int32_t mla_get_device_error(const void* workspace, int32_t* code_out, void* stream) {
+    if (!workspace || !code_out) return MLA_ERR_NULL;
+    uint32_t word = 0;
+    hipStream_t s = mla::as_stream(stream);
+    if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return MLA_ERR_DEVICE;
+    if (hipStreamSynchronize(s) != hipSuccess) return MLA_ERR_DEVICE;
+    *code_out = int32_t(word);
+    return MLA_OK;
+}
+
+int32_t mla_clear_device_error(void* workspace, void* stream) {
+    if (!workspace) return MLA_ERR_NULL;
+    hipLaunchKernelGGL(mla::clear_word_kernel, dim3(1), dim3(64), 0, mla::as_stream(stream),
+                       static_cast<uint32_t*>(workspace));
+    return mla::launch_status();
+}
+
+}  // extern "C"

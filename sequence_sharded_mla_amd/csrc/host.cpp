@@ -1,0 +1,118 @@
+// Host-only part of the library: status strings, argument validation, sizes
+// and the chunk plan.  No HIP dependency.
+#include <cmath>
+#include <cstdint>
+
+#include "plan.hpp"
+
+namespace mla {
+
+int64_t row_bytes(int32_t kv_dtype) {
+    switch (kv_dtype) {
+        case MLA_F32: return int64_t(kDk) * 4;
+        case MLA_BF16: return int64_t(kDk) * 2;
+        case MLA_FP8_DS: return int64_t(kLatent) + 4 * (kLatent / kFp8Group) + 2 * kRope;
+        default: return -1;
+    }
+}
+
+int32_t local_len(int32_t L, int32_t s, int32_t n) {
+    if (n < 1 || s < 0 || s >= n || L < 0) return -1;
+    return L > s ? (L - s + n - 1) / n : 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static bool heads_supported(int32_t h) { return h == 16 || h == 32 || h == 64 || h == 128; }
+
+int32_t validate_desc(const mla_decode_desc* d) {
+    if (!d) return MLA_ERR_NULL;
+    if (d->batch < 0 || d->q_len < 1 || d->max_blocks < 1 || d->topk < 0 || d->topk > 65536 ||
+        d->pool_blocks < 1)
+        return MLA_ERR_SHAPE;
+    if (d->kv_lora_rank != kLatent || d->rope_dim != kRope || d->block_size != kBlock)
+        return MLA_ERR_UNSUPPORTED;
+    if (!heads_supported(d->num_heads)) return MLA_ERR_UNSUPPORTED;
+    const bool f32_pair = d->q_dtype == MLA_F32 && d->kv_dtype == MLA_F32;
+    const bool bf16_q = d->q_dtype == MLA_BF16 && (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_DS);
+    if (!f32_pair && !bf16_q) return MLA_ERR_UNSUPPORTED;
+    if (d->out_dtype != MLA_F32 && d->out_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+    if (!std::isfinite(d->softmax_scale)) return MLA_ERR_SHAPE;
+    // element offsets are 64-bit in the kernels; bound the per-call rows
+    if (int64_t(d->batch) * d->q_len > (int64_t(1) << 24)) return MLA_ERR_SHAPE;
+    return MLA_OK;
+}
+
+static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan) {
+    int32_t st = validate_desc(d);
+    if (st != MLA_OK) return st;
+    if (shard_count < 1 || shard_count > 4096) return MLA_ERR_SHARD;
+    Plan p;
+    p.rows = int32_t(int64_t(shard_count) * d->batch * d->q_len);
+    if (d->topk > 0) {
+        p.n_chunks = 1;
+        p.tiles_per_chunk = 0;
+    } else {
+        // Chunk so the launch carries on the order of a thousand chunks, but
+        // never fewer than 64 tiles (4096 local tokens) per chunk: a chunk
+        // partial costs H * 513 floats written and read again, which must
+        // stay small next to the chunk's cache bytes.
+        const int64_t total_tiles = int64_t(p.rows) * d->max_blocks;
+        int64_t tpc = (total_tiles + 1023) / 1024;
+        if (tpc < 64) tpc = 64;
+        if (tpc > d->max_blocks) tpc = d->max_blocks;
+        p.tiles_per_chunk = int32_t(tpc);
+        p.n_chunks = int32_t((d->max_blocks + tpc - 1) / tpc);
+    }
+    int64_t off = kWsHeader;
+    if (p.n_chunks > 1) {
+        const int64_t slots = int64_t(p.rows) * p.n_chunks * d->num_heads;
+        p.ws_o_off = off;
+        off = align_up(off + slots * kLatent * 4, 256);
+        p.ws_lse_off = off;
+        off = align_up(off + slots * 4, 256);
+        p.ws_cnt_off = off;
+        off = align_up(off + int64_t(p.rows) * 4, 256);
+    }
+    p.ws_bytes = off;
+    *plan = p;
+    return MLA_OK;
+}
+
+}  // namespace mla
+
+extern "C" {
+
+const char* mla_status_string(int32_t status) {
+    switch (status) {
+        case MLA_OK: return "ok";
+        case MLA_ERR_NULL: return "a required pointer is NULL";
+        case MLA_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case MLA_ERR_SHARD: return "shard id, shard range or shard count is invalid";
+        case MLA_ERR_UNSUPPORTED: return "head count, dimension or dtype combination is not supported";
+        case MLA_ERR_WORKSPACE: return "workspace is smaller than mla_decode_workspace_size";
+        case MLA_ERR_DEVICE: return "a HIP runtime call failed";
+        case MLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+int32_t mla_shard_local_len(int32_t context_len, int32_t shard_id, int32_t n_shards) {
+    return mla::local_len(context_len, shard_id, n_shards);
+}
+
+int64_t mla_kv_row_bytes(int32_t kv_dtype) { return mla::row_bytes(kv_dtype); }
+
+int32_t mla_decode_workspace_size(const mla_decode_desc* desc, int32_t shard_count,
+                                  int64_t* bytes_out) {
+    if (!bytes_out) return MLA_ERR_NULL;
+    mla::Plan p;
+    int32_t st = mla::make_plan(desc, shard_count, &p);
+    if (st != MLA_OK) return st;
+    *bytes_out = p.ws_bytes;
+    return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+"""The C ABI without a GPU: exports, sizes and every host-side check.
+
+No call here reaches a kernel launch: each call carries exactly one defect
+that the host validation rejects before anything is enqueued (fake device
+addresses are never dereferenced on the host).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import sharding
+from sequence_sharded_mla_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "mla_dcp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^[a-z][\w \*]*?\b(mla_\w+)\s*\(", text, flags=re.M)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 10
+    assert set(names) == set(_lib.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.mla_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.mla_status_string(99) == b"unknown status"
+
+
+def test_local_len_matches_oracle(lib):
+    for N in (1, 2, 3, 8, 16):
+        for L in (0, 1, 2, 7, 8, 9, 1000, 32768, 1048576):
+            for s in range(N):
+                assert lib.mla_shard_local_len(L, s, N) == int(sharding.local_len(L, s, N))
+    assert lib.mla_shard_local_len(10, 3, 3) == -1
+    assert lib.mla_shard_local_len(10, -1, 3) == -1
+    assert lib.mla_shard_local_len(10, 0, 0) == -1
+    assert lib.mla_shard_local_len(-1, 0, 1) == -1
+
+
+def test_row_bytes(lib):
+    assert lib.mla_kv_row_bytes(_lib.MLA_F32) == 2304
+    assert lib.mla_kv_row_bytes(_lib.MLA_BF16) == 1152
+    assert lib.mla_kv_row_bytes(_lib.MLA_FP8_DS) == 656
+    assert lib.mla_kv_row_bytes(7) == -1
+
+
+def good_desc(**kw):
+    d = dict(batch=4, q_len=1, num_heads=64, kv_lora_rank=512, rope_dim=64, block_size=64,
+             max_blocks=16, topk=0, q_dtype=_lib.MLA_BF16, kv_dtype=_lib.MLA_FP8_DS,
+             out_dtype=_lib.MLA_BF16, softmax_scale=0.07, pool_blocks=100)
+    d.update(kw)
+    return _lib.MLADecodeDesc(**d)
+
+
+def ws_size(lib, desc, shards=1):
+    out = ctypes.c_int64(-1)
+    st = lib.mla_decode_workspace_size(ctypes.byref(desc), shards, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", -1, _lib.MLA_ERR_SHAPE),
+    ("q_len", 0, _lib.MLA_ERR_SHAPE),
+    ("max_blocks", 0, _lib.MLA_ERR_SHAPE),
+    ("topk", -1, _lib.MLA_ERR_SHAPE),
+    ("topk", 70000, _lib.MLA_ERR_SHAPE),
+    ("pool_blocks", 0, _lib.MLA_ERR_SHAPE),
+    ("kv_lora_rank", 256, _lib.MLA_ERR_UNSUPPORTED),
+    ("rope_dim", 32, _lib.MLA_ERR_UNSUPPORTED),
+    ("block_size", 16, _lib.MLA_ERR_UNSUPPORTED),
+    ("num_heads", 8, _lib.MLA_ERR_UNSUPPORTED),
+    ("num_heads", 96, _lib.MLA_ERR_UNSUPPORTED),
+    ("num_heads", 256, _lib.MLA_ERR_UNSUPPORTED),
+    ("q_dtype", _lib.MLA_FP8_DS, _lib.MLA_ERR_UNSUPPORTED),
+    ("q_dtype", _lib.MLA_F32, _lib.MLA_ERR_UNSUPPORTED),
+    ("out_dtype", _lib.MLA_FP8_DS, _lib.MLA_ERR_UNSUPPORTED),
+    ("softmax_scale", float("nan"), _lib.MLA_ERR_SHAPE),
+    ("softmax_scale", float("inf"), _lib.MLA_ERR_SHAPE),
+])
+def test_workspace_size_validates_desc(lib, field, value, code):
+    assert ws_size(lib, good_desc(**{field: value}))[0] == code
+
+
+def test_workspace_size_values(lib):
+    st, n = ws_size(lib, good_desc())
+    assert st == 0 and n >= 256 and n % 256 == 0
+    assert lib.mla_decode_workspace_size(None, 1, ctypes.byref(ctypes.c_int64())) == _lib.MLA_ERR_NULL
+    assert lib.mla_decode_workspace_size(ctypes.byref(good_desc()), 1, None) == _lib.MLA_ERR_NULL
+    assert ws_size(lib, good_desc(), 0)[0] == _lib.MLA_ERR_SHARD
+    # a long single request is split into chunks, which need scratch
+    st, n_long = ws_size(lib, good_desc(batch=1, max_blocks=4096))
+    assert st == 0 and n_long > 256
+    # f32 pair is accepted
+    assert ws_size(lib, good_desc(q_dtype=_lib.MLA_F32, kv_dtype=_lib.MLA_F32,
+                                  out_dtype=_lib.MLA_F32, num_heads=16))[0] == 0
+
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced
+
+
+def call_shards(lib, desc, **kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, ctx=FAKE, topk=None, begin=0, count=8, n=8, o=FAKE,
+             lse=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.mla_decode_partial_shards(
+        ctypes.byref(desc), v(a["q"]), v(a["kv"]), v(a["bt"]), v(a["ctx"]), v(a["topk"]),
+        a["begin"], a["count"], a["n"], v(a["o"]), v(a["lse"]), v(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.MLA_ERR_NULL),
+    (dict(kv=None), _lib.MLA_ERR_NULL),
+    (dict(bt=None), _lib.MLA_ERR_NULL),
+    (dict(ctx=None), _lib.MLA_ERR_NULL),
+    (dict(o=None), _lib.MLA_ERR_NULL),
+    (dict(lse=None), _lib.MLA_ERR_NULL),
+    (dict(ws=None), _lib.MLA_ERR_NULL),
+    (dict(topk=FAKE), _lib.MLA_ERR_SHAPE),
+    (dict(begin=1), _lib.MLA_ERR_SHARD),
+    (dict(begin=-1), _lib.MLA_ERR_SHARD),
+    (dict(count=0), _lib.MLA_ERR_SHARD),
+    (dict(n=0, count=1), _lib.MLA_ERR_SHARD),
+    (dict(q=FAKE + 8), _lib.MLA_ERR_ALIGN),
+    (dict(kv=FAKE + 4), _lib.MLA_ERR_ALIGN),
+    (dict(o=FAKE + 2), _lib.MLA_ERR_ALIGN),
+    (dict(ws=FAKE + 8), _lib.MLA_ERR_ALIGN),
+    (dict(lse=FAKE + 2), _lib.MLA_ERR_ALIGN),
+    (dict(ws_bytes=100), _lib.MLA_ERR_WORKSPACE),
+])
+def test_decode_shards_rejects(lib, kw, code):
+    assert call_shards(lib, good_desc(), **kw) == code
+
+
+def test_decode_sparse_needs_indices(lib):
+    assert call_shards(lib, good_desc(topk=2048)) == _lib.MLA_ERR_NULL
+
+
+def test_decode_desc_errors_come_first(lib):
+    assert call_shards(lib, good_desc(num_heads=48)) == _lib.MLA_ERR_UNSUPPORTED
+    assert call_shards(lib, good_desc(), q=None, n=0) == _lib.MLA_ERR_SHARD
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert call_shards(lib, good_desc(batch=0)) == 0
+
+
+def test_single_shard_entry_checks(lib):
+    d = good_desc()
+    v = ctypes.c_void_p
+    args = lambda sid, n, q=FAKE: (ctypes.byref(d), v(q), v(FAKE), v(FAKE), v(FAKE), None, sid, n,
+                                  v(FAKE), v(FAKE), v(FAKE), 1 << 30, None)
+    assert lib.mla_decode_partial(*args(8, 8)) == _lib.MLA_ERR_SHARD
+    assert lib.mla_decode_partial(*args(-1, 8)) == _lib.MLA_ERR_SHARD
+    assert lib.mla_decode_partial(*args(0, 0)) == _lib.MLA_ERR_SHARD
+    assert lib.mla_decode_partial(*args(3, 8, q=None)) == _lib.MLA_ERR_NULL
+
+
+def test_merge_and_localize_checks(lib):
+    v = ctypes.c_void_p
+    m = lambda n=4, rows=10, dv=512, pd=_lib.MLA_BF16, o=FAKE, l=FAKE, od=_lib.MLA_BF16, out=FAKE: \
+        lib.mla_lse_merge(n, rows, dv, pd, v(o), v(l), od, v(out), None, None)
+    assert m(n=0) == _lib.MLA_ERR_SHAPE
+    assert m(n=65) == _lib.MLA_ERR_SHAPE
+    assert m(rows=-1) == _lib.MLA_ERR_SHAPE
+    assert m(dv=576) == _lib.MLA_ERR_UNSUPPORTED
+    assert m(pd=_lib.MLA_FP8_DS) == _lib.MLA_ERR_UNSUPPORTED
+    assert m(od=_lib.MLA_FP8_DS) == _lib.MLA_ERR_UNSUPPORTED
+    assert m(o=None) == _lib.MLA_ERR_NULL
+    assert m(out=None) == _lib.MLA_ERR_NULL
+    assert m(o=FAKE + 4) == _lib.MLA_ERR_ALIGN
+    assert m(rows=0) == 0
+    loc = lambda cnt=10, s=0, n=8, g=FAKE, o=FAKE: lib.mla_localize_indices(v(g), cnt, s, n, v(o), None)
+    assert loc(cnt=-1) == _lib.MLA_ERR_SHAPE
+    assert loc(s=8) == _lib.MLA_ERR_SHARD
+    assert loc(n=0) == _lib.MLA_ERR_SHARD
+    assert loc(g=None) == _lib.MLA_ERR_NULL
+    assert loc(cnt=0) == 0
+    code = ctypes.c_int32()
+    assert lib.mla_get_device_error(None, ctypes.byref(code), None) == _lib.MLA_ERR_NULL
+    assert lib.mla_clear_device_error(None, None) == _lib.MLA_ERR_NULL

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Small workloads are compared element by element on every output (per-shard
+partials and merged results); they span several 64-token tiles, ragged
+tails, more shards than tokens, multi-chunk splitting and the sparse path
+with its empty-shard rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workload
+from oracle import attention, sharding
+from sequence_sharded_mla_amd import (layout, mla_clear_device_error, mla_decode_partial,
+                                      mla_get_device_error, mla_localize_indices, mla_lse_merge,
+                                      MLA_DEVERR_BLOCK_TABLE, MLA_DEVERR_INDEX)
+from sequence_sharded_mla_amd.step import ShardedDecodeStep
+
+from gpu_cases import compare, run_gpu, say, to_np, TOL_LSE, TOL_O
+
+pytestmark = pytest.mark.gpu
+
+S = workload.SPECS
+
+
+def test_tiny_f32_full():
+    x = workload.generate(S["tiny_f32"])
+    _, step = run_gpu(x)
+    errs = compare(x, step)
+    # float32 path: well inside the bar
+    assert errs["o"] < 1e-5 and errs["lse"] < 1e-5
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+def test_dense_bf16_heads(heads):
+    sp = S["dense_bf16_32k"].with_(batch=3, heads=heads, context=0, ctx_range=(1, 5000), seed=11 + heads)
+    x = workload.generate(sp)
+    _, step = run_gpu(x)
+    compare(x, step)
+
+
+def test_dense_bf16_ragged_lengths():
+    sp = S["dense_bf16_32k"].with_(batch=6, context=0, ctx_range=(1, 9), seed=3)
+    x = workload.generate(sp)   # fewer tokens than shards
+    _, step = run_gpu(x)
+    compare(x, step)
+    sp = S["dense_bf16_32k"].with_(batch=4, context=0, ctx_range=(4095, 4097 + 64 * 8), seed=4)
+    x = workload.generate(sp)
+    _, step = run_gpu(x)
+    compare(x, step)
+
+
+def test_dense_fp8_mixed_small():
+    sp = S["dense_fp8_mixed"].with_(batch=5, ctx_range=(1, 6000), seed=5)
+    x = workload.generate(sp)
+    _, step = run_gpu(x)
+    compare(x, step)
+
+
+def test_dense_fp8_multi_chunk():
+    # one long request: the shard rows are split into chunks and recombined
+    sp = S["long_fp8_1m"].with_(batch=1, context=300_001, seed=6)
+    x = workload.generate(sp)
+    _, step = run_gpu(x)
+    compare(x, step)
+
+
+def test_dense_multi_query_tokens():
+    sp = S["dense_fp8_mixed"].with_(batch=3, q_len=3, ctx_range=(3, 700), seed=7)
+    x = workload.generate(sp)
+    _, step = run_gpu(x)
+    compare(x, step)
+
+
+@pytest.mark.parametrize("n_shards", [1, 2, 3, 8, 16])
+def test_shard_counts(n_shards):
+    sp = S["dense_bf16_32k"].with_(batch=2, heads=64, n_shards=n_shards, context=0,
+                                   ctx_range=(900, 1300), seed=8 + n_shards)
+    x = workload.generate(sp)
+    _, step = run_gpu(x)
+    compare(x, step)
+    if n_shards == 1:
+        assert torch.equal(step.o_partials[0], step.o)
+
+
+def test_sparse_small():
+    sp = S["sparse_fp8_topk2048"].with_(batch=3, context=5000, topk=256, seed=9)
+    x = workload.generate(sp)
+    _, step = run_gpu(x)
+    compare(x, step)
+
+
+def test_sparse_empty_shards_and_padding():
+    sp = S["sparse_fp8_topk2048"].with_(batch=2, context=3000, topk=64, seed=10)
+    x = workload.generate(sp)
+    N = sp.n_shards
+    # request 0, token 0: every selection on shard 3; token 1: no valid entry
+    own = np.arange(3, 2998, N)[:64]
+    x.topk_idx[0, 0] = own
+    x.topk_idx[0, 1] = -1
+    x.topk_idx[1, 0, 10:] = -1
+    # rows for the newly selected positions: re-draw every stored row
+    x = _reselect(x)
+    _, step = run_gpu(x)
+    compare(x, step)
+    lse = to_np(step.lses).reshape(N, 2, 2, sp.heads)
+    for s in range(N):
+        if s != 3:
+            assert np.all(np.isneginf(lse[s, 0, 0]))
+            assert torch.count_nonzero(step.o_partials.view(N, 2, 2, sp.heads, 512)[s, 0, 0]) == 0
+    assert np.all(np.isneginf(to_np(step.lse).reshape(2, 2, sp.heads)[0, 1]))
+
+
+def _reselect(x):
+    """Regenerate stored rows after editing topk_idx (materialise the union)."""
+    sp = x.spec
+    rng = np.random.default_rng(1234)
+    pos_lists = []
+    for b in range(sp.batch):
+        sel = x.topk_idx[b].reshape(-1)
+        pos_lists.append(np.unique(sel[sel >= 0]).astype(np.int64))
+    counts = np.array([p.size for p in pos_lists])
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    T = int(offs[-1])
+    lat = rng.standard_normal((T, 512), dtype=np.float32)
+    codes, scales = workload.quantize_fp8_groups(lat)
+    rope = workload._bf16_bits(rng.standard_normal((T, 64), dtype=np.float32))
+    x.row_offsets, x.row_pos = offs, np.concatenate(pos_lists)
+    x.latent, x.scales, x.rope = codes, scales, rope
+    return x
+
+
+def test_single_shard_entry_matches_shards_call():
+    sp = S["dense_fp8_mixed"].with_(batch=3, ctx_range=(100, 3000), seed=12)
+    x = workload.generate(sp)
+    cache, step = run_gpu(x)
+    d = cache.desc
+    from sequence_sharded_mla_amd import alloc_workspace
+    ws = alloc_workspace(d, 1)
+    for s in (0, 5):
+        o = torch.empty_like(step.o_partials[s])
+        l = torch.empty_like(step.lses[s])
+        mla_decode_partial(d, cache.q, cache.pool, cache.block_tables[s].contiguous(),
+                           cache.context_lens, None, s, sp.n_shards, o, l, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, step.o_partials[s]) and torch.equal(l, step.lses[s])
+
+
+def test_bitwise_reproducible():
+    sp = S["dense_fp8_mixed"].with_(batch=4, ctx_range=(1000, 9000), seed=13)
+    x = workload.generate(sp)
+    cache, step = run_gpu(x)
+    o1, l1 = step.o.clone(), step.lse.clone()
+    p1 = step.o_partials.clone()
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, step.o) and torch.equal(l1, step.lse) and torch.equal(p1, step.o_partials)
+
+
+def test_lse_merge_entry():
+    rng = np.random.default_rng(14)
+    n, rows = 8, 300
+    o = rng.standard_normal((n, rows, 512)).astype(np.float32)
+    l = (rng.standard_normal((n, rows)) * 5).astype(np.float32)
+    l[:, :7] = -np.inf            # all parts empty
+    l[2:, 7:20] = -np.inf         # some parts empty
+    o[2:, 7:20] = np.nan          # empty parts' outputs are never read
+    for pd in (torch.float32, torch.bfloat16):
+        ot = torch.from_numpy(o).cuda().to(pd)
+        src = ot.float().cpu().numpy().astype(np.float64)
+        ref_o, ref_l = attention.merge(np.nan_to_num(src), l.astype(np.float64))
+        out = torch.empty((rows, 512), dtype=torch.bfloat16, device="cuda")
+        lo = torch.empty(rows, dtype=torch.float32, device="cuda")
+        mla_lse_merge(ot, torch.from_numpy(l).cuda(), out, lo)
+        torch.cuda.synchronize()
+        got = to_np(out)
+        assert not np.isnan(got).any()
+        assert np.abs(got - ref_o).max() <= 2 ** -8 * max(1.0, np.abs(ref_o).max())
+        gl = lo.cpu().numpy()
+        assert np.array_equal(np.isneginf(gl), np.isneginf(ref_l))
+        fin = np.isfinite(ref_l)
+        assert np.abs(gl[fin] - ref_l[fin]).max() < 1e-5
+
+
+def test_localize_bit_exact():
+    rng = np.random.default_rng(15)
+    g = rng.integers(-5, 1 << 20, size=300_001).astype(np.int32)
+    gt = torch.from_numpy(g).cuda()
+    out = torch.empty_like(gt)
+    for N in (1, 3, 8):
+        for s in range(N):
+            mla_localize_indices(gt, s, N, out)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), sharding.localize(g, s, N))
+
+
+def test_device_error_narrow_block_table():
+    sp = S["dense_bf16_32k"].with_(batch=2, heads=64, context=0, ctx_range=(3000, 3000), seed=16)
+    x = workload.generate(sp)
+    cache = layout.pack(x, device="cuda")
+    # a table one block too narrow for the longest shard
+    narrow = cache.block_tables[:, :, :-1].contiguous()
+    cache.block_tables = narrow
+    cache.desc.max_blocks = narrow.shape[2]
+    step = ShardedDecodeStep(cache, sp.out_dtype)
+    step()
+    torch.cuda.synchronize()
+    assert mla_get_device_error(step.workspace) & MLA_DEVERR_BLOCK_TABLE
+    mla_clear_device_error(step.workspace)
+    assert mla_get_device_error(step.workspace) == 0
+
+
+def test_device_error_index_beyond_prefix():
+    sp = S["sparse_fp8_topk2048"].with_(batch=1, context=1000, topk=16, seed=17)
+    x = workload.generate(sp)
+    cache = layout.pack(x, device="cuda")
+    bad = cache.topk_idx.clone()
+    bad[0, 0, 0] = 999  # query 0 sees positions 0..998
+    cache.topk_idx = bad
+    step = ShardedDecodeStep(cache, sp.out_dtype)
+    step()
+    torch.cuda.synchronize()
+    assert mla_get_device_error(step.workspace) & MLA_DEVERR_INDEX
+    # the offending entry is skipped: result equals the oracle without it
+    x.topk_idx = bad.cpu().numpy()
+    x.topk_idx[0, 0, 0] = -1
+    mla_clear_device_error(step.workspace)
+    compare(x, step)
