@@ -3,6 +3,7 @@
 
 #include "../../include/mla_dcp.h"
 #include "common.hpp"
+#include "decode_mfma.hpp"
 #include "decode_valu.hpp"
 #include "params.hpp"
 #include "plan.hpp"
@@ -67,17 +68,23 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     p.scale = d->softmax_scale;
 
     hipStream_t s = as_stream(stream);
-    const dim3 grid(uint32_t(plan.rows) * plan.n_chunks, uint32_t(d->num_heads / valu::kHeads));
-    switch (d->kv_dtype) {
-        case MLA_F32:
-            hipLaunchKernelGGL(valu::decode_valu_kernel<MLA_F32>, grid, dim3(valu::kThreads), 0, s, p);
-            break;
-        case MLA_BF16:
-            hipLaunchKernelGGL(valu::decode_valu_kernel<MLA_BF16>, grid, dim3(valu::kThreads), 0, s, p);
-            break;
-        default:
-            hipLaunchKernelGGL(valu::decode_valu_kernel<MLA_FP8_DS>, grid, dim3(valu::kThreads), 0, s, p);
-            break;
+    const uint32_t n_items = uint32_t(plan.rows) * plan.n_chunks;
+    const bool mfma_bf16 = d->kv_dtype == MLA_BF16 && d->topk == 0 && d->num_heads == 128;
+    if (mfma_bf16) {
+        hipLaunchKernelGGL(mfma::decode_mfma_bf16_kernel<4>, dim3(n_items), dim3(256), 0, s, p);
+    } else {
+        const dim3 grid(n_items, uint32_t(d->num_heads / valu::kHeads));
+        switch (d->kv_dtype) {
+            case MLA_F32:
+                hipLaunchKernelGGL(valu::decode_valu_kernel<MLA_F32>, grid, dim3(valu::kThreads), 0, s, p);
+                break;
+            case MLA_BF16:
+                hipLaunchKernelGGL(valu::decode_valu_kernel<MLA_BF16>, grid, dim3(valu::kThreads), 0, s, p);
+                break;
+            default:
+                hipLaunchKernelGGL(valu::decode_valu_kernel<MLA_FP8_DS>, grid, dim3(valu::kThreads), 0, s, p);
+                break;
+        }
     }
     if ((st = launch_status()) != MLA_OK) return st;
     if (plan.n_chunks > 1) {

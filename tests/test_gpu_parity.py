@@ -226,3 +226,45 @@ def test_device_error_index_beyond_prefix():
     x.topk_idx[0, 0, 0] = -1
     mla_clear_device_error(step.workspace)
     compare(x, step)
+
+
+def test_bf16_h128_bitwise_reproducible_and_chunked():
+    # one long request forces several chunks per shard row (chunk combine)
+    sp = S["dense_bf16_32k"].with_(batch=1, context=600_000, seed=18)
+    x = workload.generate(sp)
+    cache, step = run_gpu(x)
+    compare(x, step)
+    o1, p1 = step.o.clone(), step.o_partials.clone()
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, step.o) and torch.equal(p1, step.o_partials)
+
+
+@pytest.mark.parametrize("heads", [64, 128])
+def test_bad_block_id_is_skipped(heads):
+    sp = S["dense_bf16_32k"].with_(batch=2, heads=heads, context=0, ctx_range=(5000, 5000), seed=19)
+    x = workload.generate(sp)
+    cache = layout.pack(x, device="cuda")
+    N = sp.n_shards
+    bt = cache.block_tables.clone()
+    bt[2, 0, 3] = -7                     # shard 2, request 0, local block 3
+    bt[5, 1, 0] = cache.pool_blocks      # shard 5, request 1, local block 0
+    cache.block_tables = bt
+    step = ShardedDecodeStep(cache, sp.out_dtype)
+    step()
+    torch.cuda.synchronize()
+    assert mla_get_device_error(step.workspace) & MLA_DEVERR_BLOCK_TABLE
+    from oracle import decode as odecode
+    q = odecode.query_to_f64(x.q, sp.q_dtype)
+    rows = odecode.storage_rows(sp.kv_dtype, x.latent, x.scales, x.rope, x.row_offsets, x.row_pos)
+    H = sp.heads
+    o_sh = to_np(step.o_partials).reshape(N, 2, H, 512)
+    l_sh = to_np(step.lses).reshape(N, 2, H)
+    for s, b, blk in ((2, 0, 3), (5, 1, 0)):
+        L = int(x.context_lens[b])
+        owned = [p for p in range(L) if p % N == s and not (blk * 64 <= p // N < blk * 64 + 64)]
+        lat, rope = rows(b, np.array(owned))
+        k = np.concatenate([lat, rope], axis=1)
+        o_ref, l_ref = attention.attend(q[b, 0], k, lat, sp.scale)
+        assert np.abs(o_sh[s, b] - o_ref).max() <= TOL_O
+        assert np.abs(l_sh[s, b] - l_ref).max() <= TOL_LSE
