@@ -105,7 +105,7 @@ typedef struct mla_decode_desc {
     int32_t q_dtype;      /* MLA_F32 (with MLA_F32 cache) or MLA_BF16       */
     int32_t kv_dtype;     /* MLA_F32, MLA_BF16 or MLA_FP8_DS                */
     int32_t out_dtype;    /* MLA_F32 or MLA_BF16                            */
-    float softmax_scale;  /* finite; scores are scale * q.k                 */
+    float softmax_scale;  /* finite and > 0; scores are scale * q.k         */
     int64_t pool_blocks;  /* number of blocks in kv_pool, >= 1              */
 } mla_decode_desc;
 

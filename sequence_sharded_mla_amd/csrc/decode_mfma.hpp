@@ -47,12 +47,18 @@ constexpr int kInstPerSub = kSubB / 1024;  // 36 wave-wide 16 B loads
 constexpr int kQSteps = kDk / 16;        // 36 K-steps of the score product
 constexpr int kDvTiles = kLatent / 32;   // 16 32-dim tiles of the output
 
-// 3-bit row swizzle: rows t..t+7 (t % 8 == 0) map to 8 distinct values, and
-// rows t..t+3 (t % 4 == 0) to values distinct in bits 1..2.
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
-
-// byte offset of 16-byte chunk c of row t inside a sub-tile
-__device__ __forceinline__ int chunk_off(int t, int c) { return t * kRowB + ((c ^ swz(t)) << 4); }
+// Row swizzle of the 16-byte chunks in LDS.  Chunk c of row t is stored at
+// position c ^ f(t) with f(t) = ((t & 3) << 2) | ((t >> 2) & 3): the XOR only
+// flips the low 4 bits, so chunks stay inside their aligned 256-byte group.
+// The last 8 chunks of a row (the rope part) use f(t) & 7 to stay inside
+// the row.  With 64 four-byte banks this makes the 16-lane passes of the
+// K-row reads (16 rows, one chunk each) and the 32-lane passes of the V^T
+// transposing reads (8 rows x 4 chunk halves) hit every bank once.
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+__device__ __forceinline__ int swz_pos(int t, int c) {
+    const int f = swz(t);
+    return c < 64 ? (c ^ f) : (c ^ (f & 7));
+}
 
 // vmcnt-only wait (expcnt / lgkmcnt left at their maxima), gfx9 encoding
 template <int N>
@@ -108,9 +114,25 @@ __device__ __forceinline__ void mfma32_acc_lead(f32x16& c, const bf16x8& a, cons
 // accumulators (the compiler does not see the asm as an MFMA).
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
 
+constexpr int kQLatSteps = kLatent / 16;  // 32 K-steps over the latent dims
+constexpr int kQRopeB = 128 * kRope * 2;    // rope part of Q for 128 heads
+
 struct alignas(16) SmemBf16 {
     uint8_t ring[kRing][kSubB];
+    uint8_t qrope[kQRopeB];  // [head][8 chunks of 16 B], chunk c at c ^ ((head >> 1) & 7)
 };
+
+// max / sum of x over lanes i and i ^ 32 (one cross-half VALU swap)
+__device__ __forceinline__ float xhalf_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Per-lane byte offsets (inside a sub-tile) of this wave's LPW direct-to-LDS
 // loads: load k of wave w fills LDS bytes [(k*NW + w) * 1024, +1024), 16 bytes
@@ -122,25 +144,25 @@ __device__ __forceinline__ int dma_offset(int k, int wave, int lane, int valid) 
     const int u = ins * 64 + lane;
     const int t = u / kChunks;
     const int pos = u - t * kChunks;
-    const int c = pos ^ swz(t);
+    const int c = swz_pos(t, pos);  // the swizzle is its own inverse
     const int tr = t < valid ? t : valid - 1;
     return tr * kRowB + c * 16;
 }
 
-// One wave-wide direct-to-LDS load: lane i copies 16 bytes from gptr (its
-// own address) to LDS byte lds_base + 16 i.  Issued as inline asm so the
+// One wave-wide direct-to-LDS load: lane i copies 16 bytes from
+// gbase + voff(i) (gbase uniform, in SGPRs) to LDS byte lds_base + 16 i.  Issued as inline asm so the
 // compiler does not see an LDS write in flight: it would otherwise wait for
 // every outstanding load (vmcnt 0) before each LDS transpose read.  The
 // waits that order these loads before their LDS readers are explicit
 // (wait_vm + barrier).  M0 holds the LDS base; writing M0 needs one wait
 // state before the load.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+__device__ __forceinline__ void dma16(const void* gbase, int voff, uint32_t lds_base) {
     asm volatile(
-        "s_mov_b32 m0, %1\n\t"
+        "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, off"
+        "global_load_lds_dwordx4 %0, %1"
         :
-        : "v"(gptr), "s"(lds_base)
+        : "v"(voff), "s"(gbase), "s"(lds_base)
         : "memory", "m0");
 }
 
@@ -155,7 +177,7 @@ __device__ __forceinline__ void issue_sub(uint8_t* dst, const uint8_t* src, cons
     const uint32_t base = lds_addr(dst);
 #pragma unroll
     for (int k = 0; k < LPW; ++k)
-        dma16(src + offs[k], __builtin_amdgcn_readfirstlane(base + (k * NW + wave) * 1024));
+        dma16(src, offs[k], __builtin_amdgcn_readfirstlane(base + (k * NW + wave) * 1024));
 }
 
 template <int NW>
@@ -165,7 +187,7 @@ __device__ __forceinline__ void issue_sub_tail(uint8_t* dst, const uint8_t* src,
     const uint32_t base = lds_addr(dst);
 #pragma unroll
     for (int k = 0; k < LPW; ++k)
-        dma16(src + dma_offset<NW>(k, wave, lane, valid),
+        dma16(src, dma_offset<NW>(k, wave, lane, valid),
               __builtin_amdgcn_readfirstlane(base + (k * NW + wave) * 1024));
 }
 
@@ -221,12 +243,22 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodePara
     const int n_sub = tok1 > tok0 ? (tok1 - tok0 + kSub - 1) / kSub : 0;
 
     // ---- Q^T fragments: head `head`, dims 16 ks + 8 half .. + 8 ------------
-    bf16x8 qf[kQSteps];
+    // latent part in registers, rope part in LDS (each wave writes and later
+    // reads only its own heads, so program order within the wave suffices)
+    bf16x8 qf[kQLatSteps];
+    const int qr_off = head * (kRope * 2);
+    const int qr_sw = (head >> 1) & 7;
     {
         const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
             static_cast<const uint16_t*>(p.q) + ((size_t(id.b) * p.Tq + id.t) * p.H + head) * kDk);
 #pragma unroll
-        for (int ks = 0; ks < kQSteps; ++ks) qf[ks] = qrow[2 * ks + half];
+        for (int ks = 0; ks < kQLatSteps; ++ks) qf[ks] = qrow[2 * ks + half];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = 2 * u + half;
+            *(MLA_LDS bf16x8*)((MLA_LDS uint8_t*)sm.qrope + qr_off + ((c ^ qr_sw) << 4)) =
+                qrow[2 * (kQLatSteps + u) + half];
+        }
     }
 
     int offs[LPW];
@@ -275,26 +307,26 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodePara
     const float sl2 = p.scale * 1.4426950408889634f;
     bool bad_block = false;
 
-    // per-lane operand addresses inside a sub-tile.  A chunk index c = 8g + c'
-    // (c' < 8) lands at 8g + (c' ^ swz), so every read is one of a few
-    // per-lane bases plus the compile-time offset 128 g.
-    int kb[4];  // K rows: chunk 2 ks + half, ks = 4 g + u
+    // per-lane operand addresses inside a sub-tile: every read is one of a
+    // few per-lane bases plus a compile-time offset
+    int kb[8];  // K rows, latent chunks c = 2 ks + half = 16 g + c', ks = 8 g + u
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kb[u] = col * kRowB + (((2 * u + half) ^ swz(col)) << 4);
-    int vb[2][2][2];  // V^T reads: [token half jj][row t1 / t2][mt parity]
+    for (int u = 0; u < 8; ++u) kb[u] = col * kRowB + (((2 * u + half) ^ swz(col)) << 4);
+    int kr[4];  // K rows, rope chunks 64 .. 71
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kr[u] = col * kRowB + (swz_pos(col, 64 + 2 * u + half) << 4);
+    int vb[2][4];  // V^T reads: [row t / t + 8][mt & 3]; token half jj adds 16 rows
     {
         const int g16 = lane >> 4, s16 = lane & 15;
         const int c0 = 2 * (g16 & 1) + ((s16 & 3) >> 1);  // chunk within a 32-dim tile
         const int bsub = (s16 & 1) * 8;                  // byte within the chunk
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int w = 0; w < 2; ++w) {
+            const int t = 4 * (g16 >> 1) + (s16 >> 2) + 8 * w;
 #pragma unroll
-            for (int w = 0; w < 2; ++w) {
-                const int t = 16 * jj + 4 * (g16 >> 1) + (s16 >> 2) + 8 * w;
-#pragma unroll
-                for (int par = 0; par < 2; ++par)
-                    vb[jj][w][par] = t * kRowB + bsub + (((4 * par + c0) ^ swz(t)) << 4);
-            }
+            for (int q = 0; q < 4; ++q)
+                vb[w][q] = t * kRowB + bsub + (((4 * q + c0) ^ swz(t)) << 4);
+        }
     }
 
     for (int j = 0; j < n_sub; ++j) {
@@ -312,30 +344,49 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodePara
         f32x16 st;
         const MLA_LDS uint8_t* lt = (const MLA_LDS uint8_t*)tile;
         auto kread = [&](int ks) -> bf16x8 {
-            return *(const MLA_LDS bf16x8*)(lt + kb[ks & 3] + 128 * (ks >> 2));
+            const int a = ks < 32 ? kb[ks & 7] + 256 * (ks >> 3) : kr[ks - 32];
+            return *(const MLA_LDS bf16x8*)(lt + a);
         };
-        // K fragments are read two steps ahead of the MFMA that uses them
-        bf16x8 kf0 = kread(0), kf1 = kread(1), kf2;
+        auto qread = [&](int u) -> bf16x8 {
+            return *(const MLA_LDS bf16x8*)((const MLA_LDS uint8_t*)sm.qrope + qr_off +
+                                            (((2 * u + half) ^ qr_sw) << 4));
+        };
+        // K fragments are read four steps ahead of the MFMA that uses them
+        constexpr int kAheadK = 4;
+        bf16x8 kf[kAheadK + 1];
+        bf16x8 qrf[4];
+#pragma unroll
+        for (int i = 0; i < kAheadK; ++i) kf[i] = kread(i);
 #pragma unroll
         for (int ks = 0; ks < kQSteps; ++ks) {
-            if (ks + 2 < kQSteps) kf2 = kread(ks + 2);
-            if (ks == 0) mfma32_v_first(st, kf0, qf[ks]);
-            else if (ks == kQSteps - 1) mfma32_v_last(st, kf0, qf[ks]);
-            else mfma32_v(st, kf0, qf[ks]);
-            kf0 = kf1;
-            kf1 = kf2;
+            if (ks + kAheadK < kQSteps) kf[(ks + kAheadK) % (kAheadK + 1)] = kread(ks + kAheadK);
+            if (ks == kQLatSteps - 8) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) qrf[u] = qread(u);
+            }
+            const bf16x8& a = kf[ks % (kAheadK + 1)];
+            const bf16x8& b = ks < kQLatSteps ? qf[ks] : qrf[ks - kQLatSteps];
+            if (ks == 0) mfma32_v_first(st, a, b);
+            else if (ks == kQSteps - 1) mfma32_v_last(st, a, b);
+            else mfma32_v(st, a, b);
         }
 
         // ---- online softmax (log2 domain, lagging reference max) ----------
-        float mx = -INFINITY;
+        // raw scores are scaled inside the exponent (scale > 0 keeps the
+        // order, so the max is taken on raw scores); only a partial last
+        // sub-tile needs masking
+        if (cnt < kSub) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int tok = (i >> 2) * 8 + half * 4 + (i & 3);
-            const float v = tok < cnt ? st[i] * sl2 : -INFINITY;
-            st[i] = v;
-            mx = fmaxf(mx, v);
+            for (int i = 0; i < 16; ++i) {
+                const int tok = (i >> 2) * 8 + half * 4 + (i & 3);
+                if (tok >= cnt) st[i] = -INFINITY;
+            }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float mx = fmaxf(fmaxf(st[0], st[1]), st[2]);
+#pragma unroll
+        for (int i = 3; i < 16; i += 2) mx = fmaxf(fmaxf(mx, st[i]), st[i + 1]);
+        mx = fmaxf(mx, st[15]);
+        mx = xhalf_max(mx) * sl2;
         if (m == -INFINITY) {
             m = mx;  // first scores of this head: nothing accumulated yet
         } else if (__any(mx > m + kLag)) {
@@ -346,14 +397,16 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodePara
             l *= alpha;
             m = m_new;
         }
+        // with no valid score yet (m = -inf) every term is 0
+        const float nm = (m == -INFINITY) ? 0.f : -m;
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float e = (st[i] == -INFINITY) ? 0.f : exp2f(st[i] - m);
+            const float e = __builtin_amdgcn_exp2f(fmaf(st[i], sl2, nm));
             st[i] = e;
             ps += e;
         }
-        ps += __shfl_xor(ps, 32);
+        ps = xhalf_sum(ps);
         l += ps;
         bf16x8 pf[2];
 #pragma unroll
@@ -365,11 +418,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodePara
         // V^T fragment of 32-dim tile mt and 16-token half jj: two transposing
         // reads of 4 tokens x 4 dims per 16-lane group
         auto vread = [&](int jj, int mt) -> bf16x8 {
-            const int go = 128 * (mt >> 1);
+            const int go = 256 * (mt >> 2) + jj * 16 * kRowB;
             const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (MLA_LDS s16x4*)(lt + vb[jj][0][mt & 1] + go));
+                (MLA_LDS s16x4*)(lt + vb[0][mt & 3] + go));
             const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (MLA_LDS s16x4*)(lt + vb[jj][1][mt & 1] + go));
+                (MLA_LDS s16x4*)(lt + vb[1][mt & 3] + go));
             i32x4 raw;
             raw[0] = (int)(uint16_t)r1[0] | ((int)(uint16_t)r1[1] << 16);
             raw[1] = (int)(uint16_t)r1[2] | ((int)(uint16_t)r1[3] << 16);
@@ -377,19 +430,24 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodePara
             raw[3] = (int)(uint16_t)r2[2] | ((int)(uint16_t)r2[3] << 16);
             return __builtin_bit_cast(bf16x8, raw);
         };
-        // V^T fragments of tile mt + 1 are read while tile mt multiplies
-        bf16x8 va0 = vread(0, 0), va1 = vread(1, 0), vb0, vb1;
+        // V^T fragments are read two output tiles ahead of their MFMAs
+        constexpr int kAheadV = 2;
+        bf16x8 vf[kAheadV + 1][2];
+#pragma unroll
+        for (int i = 0; i < kAheadV; ++i) {
+            vf[i][0] = vread(0, i);
+            vf[i][1] = vread(1, i);
+        }
 #pragma unroll
         for (int mt = 0; mt < kDvTiles; ++mt) {
-            if (mt + 1 < kDvTiles) {
-                vb0 = vread(0, mt + 1);
-                vb1 = vread(1, mt + 1);
+            if (mt + kAheadV < kDvTiles) {
+                vf[(mt + kAheadV) % (kAheadV + 1)][0] = vread(0, mt + kAheadV);
+                vf[(mt + kAheadV) % (kAheadV + 1)][1] = vread(1, mt + kAheadV);
             }
-            if (mt == 0) mfma32_acc_lead(acc[mt], va0, pf[0]);
-            else mfma32_acc(acc[mt], va0, pf[0]);
-            mfma32_acc(acc[mt], va1, pf[1]);
-            va0 = vb0;
-            va1 = vb1;
+            const int r = mt % (kAheadV + 1);
+            if (mt == 0) mfma32_acc_lead(acc[mt], vf[r][0], pf[0]);
+            else mfma32_acc(acc[mt], vf[r][0], pf[0]);
+            mfma32_acc(acc[mt], vf[r][1], pf[1]);
         }
     }
     mfma_drain();

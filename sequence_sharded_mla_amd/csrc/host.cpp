@@ -37,7 +37,7 @@ int32_t validate_desc(const mla_decode_desc* d) {
     const bool bf16_q = d->q_dtype == MLA_BF16 && (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_DS);
     if (!f32_pair && !bf16_q) return MLA_ERR_UNSUPPORTED;
     if (d->out_dtype != MLA_F32 && d->out_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
-    if (!std::isfinite(d->softmax_scale)) return MLA_ERR_SHAPE;
+    if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return MLA_ERR_SHAPE;
     // element offsets are 64-bit in the kernels; bound the per-call rows
     if (int64_t(d->batch) * d->q_len > (int64_t(1) << 24)) return MLA_ERR_SHAPE;
     return MLA_OK;

@@ -94,6 +94,8 @@ def ws_size(lib, desc, shards=1):
     ("out_dtype", _lib.MLA_FP8_DS, _lib.MLA_ERR_UNSUPPORTED),
     ("softmax_scale", float("nan"), _lib.MLA_ERR_SHAPE),
     ("softmax_scale", float("inf"), _lib.MLA_ERR_SHAPE),
+    ("softmax_scale", 0.0, _lib.MLA_ERR_SHAPE),
+    ("softmax_scale", -0.1, _lib.MLA_ERR_SHAPE),
 ])
 def test_workspace_size_validates_desc(lib, field, value, code):
     assert ws_size(lib, good_desc(**{field: value}))[0] == code
