@@ -3,6 +3,7 @@
 
 #include "../../include/mla_dcp.h"
 #include "common.hpp"
+#include "decode_fp8.hpp"
 #include "decode_mfma.hpp"
 #include "decode_valu.hpp"
 #include "params.hpp"
@@ -70,8 +71,23 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     hipStream_t s = as_stream(stream);
     const uint32_t n_items = uint32_t(plan.rows) * plan.n_chunks;
     const bool mfma_bf16 = d->kv_dtype == MLA_BF16 && d->topk == 0 && d->num_heads == 128;
+    const bool mfma_fp8 = d->kv_dtype == MLA_FP8_DS && (d->num_heads == 64 || d->num_heads == 128) &&
+                          d->topk <= mfma::kMaxTopk;
     if (mfma_bf16) {
         hipLaunchKernelGGL(mfma::decode_mfma_bf16_kernel<4>, dim3(n_items), dim3(256), 0, s, p);
+    } else if (mfma_fp8) {
+        const bool sparse = d->topk > 0;
+        if (d->num_heads == 64) {
+            if (sparse)
+                hipLaunchKernelGGL((mfma::decode_mfma_fp8_kernel<2, true>), dim3(n_items), dim3(128), 0, s, p);
+            else
+                hipLaunchKernelGGL((mfma::decode_mfma_fp8_kernel<2, false>), dim3(n_items), dim3(128), 0, s, p);
+        } else {
+            if (sparse)
+                hipLaunchKernelGGL((mfma::decode_mfma_fp8_kernel<4, true>), dim3(n_items), dim3(256), 0, s, p);
+            else
+                hipLaunchKernelGGL((mfma::decode_mfma_fp8_kernel<4, false>), dim3(n_items), dim3(256), 0, s, p);
+        }
     } else {
         const dim3 grid(n_items, uint32_t(d->num_heads / valu::kHeads));
         switch (d->kv_dtype) {

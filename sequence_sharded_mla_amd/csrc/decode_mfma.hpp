@@ -24,20 +24,12 @@
 #pragma once
 
 #include "common.hpp"
+#include "mfma_common.hpp"
 #include "params.hpp"
 
 namespace mla {
 namespace mfma {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(2))) int i32x2;
-typedef __attribute__((ext_vector_type(4))) int i32x4;
-
-#define MLA_LDS __attribute__((address_space(3)))
-
-constexpr int kSub = 32;                 // tokens per sub-tile
 constexpr int kRing = 4;                 // sub-tiles resident in LDS
 constexpr int kAhead = kRing - 1;        // sub-tiles in flight ahead of compute
 constexpr int kRowB = kDk * 2;           // 1152 B per bf16 row
@@ -45,7 +37,6 @@ constexpr int kChunks = kRowB / 16;      // 72 16-byte chunks per row
 constexpr int kSubB = kSub * kRowB;      // 36864 B per sub-tile
 constexpr int kInstPerSub = kSubB / 1024;  // 36 wave-wide 16 B loads
 constexpr int kQSteps = kDk / 16;        // 36 K-steps of the score product
-constexpr int kDvTiles = kLatent / 32;   // 16 32-dim tiles of the output
 
 // Row swizzle of the 16-byte chunks in LDS.  Chunk c of row t is stored at
 // position c ^ f(t) with f(t) = ((t & 3) << 2) | ((t >> 2) & 3): the XOR only
@@ -60,13 +51,6 @@ __device__ __forceinline__ int swz_pos(int t, int c) {
     return c < 64 ? (c ^ f) : (c ^ (f & 7));
 }
 
-// vmcnt-only wait (expcnt / lgkmcnt left at their maxima), gfx9 encoding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 template <int LPW>
 __device__ __forceinline__ void wait_outstanding(int subs) {
     // subs sub-tiles may stay in flight; each is LPW loads of this wave, and
@@ -77,62 +61,12 @@ __device__ __forceinline__ void wait_outstanding(int subs) {
     else wait_vm<0>();
 }
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Score-product MFMAs with the accumulator in VGPRs.  The output
-// accumulators fill the AGPR file, and the compiler would otherwise place
-// this accumulator there too and shuttle output tiles through VGPRs.
-// Back-to-back accumulation into the same registers needs no wait states;
-// the last MFMA of a chain is followed by enough NOPs for a VALU read of the
-// result (an 8-pass XDL write needs 11).
-__device__ __forceinline__ void mfma32_v_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma32_v(f32x16& c, const bf16x8& a, const bf16x8& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma32_v_last(f32x16& c, const bf16x8& a, const bf16x8& b) {
-    asm volatile(
-        "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
-        "s_nop 7\n\ts_nop 7\n\ts_nop 7"
-        : "+v"(c)
-        : "v"(a), "v"(b));
-}
-
-// Output-product MFMA with the accumulator pinned to AGPRs.  Issued as
-// inline asm so the whole 256-register output accumulator stays in the AGPR
-// file; `lead_nops` covers a VALU write of the B operand just before.
-__device__ __forceinline__ void mfma32_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma32_acc_lead(f32x16& c, const bf16x8& a, const bf16x8& b) {
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-// Wait states after the last asm MFMA writes before ordinary code reads the
-// accumulators (the compiler does not see the asm as an MFMA).
-__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
-
-constexpr int kQLatSteps = kLatent / 16;  // 32 K-steps over the latent dims
 constexpr int kQRopeB = 128 * kRope * 2;    // rope part of Q for 128 heads
 
 struct alignas(16) SmemBf16 {
     uint8_t ring[kRing][kSubB];
     uint8_t qrope[kQRopeB];  // [head][8 chunks of 16 B], chunk c at c ^ ((head >> 1) & 7)
 };
-
-// max / sum of x over lanes i and i ^ 32 (one cross-half VALU swap)
-__device__ __forceinline__ float xhalf_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xhalf_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Per-lane byte offsets (inside a sub-tile) of this wave's LPW direct-to-LDS
 // loads: load k of wave w fills LDS bytes [(k*NW + w) * 1024, +1024), 16 bytes
@@ -147,27 +81,6 @@ __device__ __forceinline__ int dma_offset(int k, int wave, int lane, int valid) 
     const int c = swz_pos(t, pos);  // the swizzle is its own inverse
     const int tr = t < valid ? t : valid - 1;
     return tr * kRowB + c * 16;
-}
-
-// One wave-wide direct-to-LDS load: lane i copies 16 bytes from
-// gbase + voff(i) (gbase uniform, in SGPRs) to LDS byte lds_base + 16 i.  Issued as inline asm so the
-// compiler does not see an LDS write in flight: it would otherwise wait for
-// every outstanding load (vmcnt 0) before each LDS transpose read.  The
-// waits that order these loads before their LDS readers are explicit
-// (wait_vm + barrier).  M0 holds the LDS base; writing M0 needs one wait
-// state before the load.
-__device__ __forceinline__ void dma16(const void* gbase, int voff, uint32_t lds_base) {
-    asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, %1"
-        :
-        : "v"(voff), "s"(gbase), "s"(lds_base)
-        : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return uint32_t(reinterpret_cast<uintptr_t>((const MLA_LDS void*)p));
 }
 
 template <int NW>
@@ -190,30 +103,6 @@ __device__ __forceinline__ void issue_sub_tail(uint8_t* dst, const uint8_t* src,
         dma16(src, dma_offset<NW>(k, wave, lane, valid),
               __builtin_amdgcn_readfirstlane(base + (k * NW + wave) * 1024));
 }
-
-// acc *= a for one 16-register accumulator tile held in AGPRs.  Written as
-// register moves + a multiply so the accumulators never leave the AGPR file.
-__device__ __forceinline__ void scale_acc(f32x16& acc, float a) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        float x = acc[e];
-        float tmp;
-        asm volatile(
-            "v_accvgpr_read_b32 %1, %0\n\t"
-            "v_mul_f32 %1, %1, %2\n\t"
-            "v_accvgpr_write_b32 %0, %1"
-            : "+a"(x), "=&v"(tmp)
-            : "v"(a));
-        acc[e] = x;
-    }
-}
-
-// Growth of a head's running max (log2 units) tolerated before the
-// accumulators are rescaled: probabilities are formed against a reference
-// max that may lag the true running max by at most this much, so they stay
-// below 2^kLag; O and the normaliser share the reference, so the result is
-// unchanged.
-constexpr float kLag = 8.f;
 
 template <int NW>
 __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodeParams p) {
@@ -266,10 +155,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodePara
     for (int k = 0; k < LPW; ++k) offs[k] = dma_offset<NW>(k, wave, lane, kSub);
 
     // first row of sub-tile j and its real row count.  A bad block id gives
-    // valid = 0: the loads then re-read this row's query (a finite 1152-byte
-    // row) and every score of the sub-tile is masked.
-    const uint8_t* qrow_bytes = reinterpret_cast<const uint8_t*>(
-        static_cast<const uint16_t*>(p.q) + (size_t(id.b) * p.Tq + id.t) * p.H * kDk);
+    // valid = 0: the loads then re-read the zero row and every score of the
+    // sub-tile is masked.
     // block ids are read through the scalar cache (the table is read-only
     // here): a vector load would need a vmcnt wait that drains the ring
     const __attribute__((address_space(4))) int32_t* btc =
@@ -280,7 +167,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodePara
         const int32_t blk = btc[j0 / kBlock];
         if (blk < 0 || blk >= p.pool_blocks) {
             valid = 0;
-            return qrow_bytes;
+            return kZeroRow;
         }
         return p.kv + (int64_t(blk) * kBlock + (j0 % kBlock)) * kRowB;
     };
@@ -445,7 +332,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodePara
                 vf[(mt + kAheadV) % (kAheadV + 1)][1] = vread(1, mt + kAheadV);
             }
             const int r = mt % (kAheadV + 1);
-            if (mt == 0) mfma32_acc_lead(acc[mt], vf[r][0], pf[0]);
+            if (mt == 0) mfma32_acc<true>(acc[mt], vf[r][0], pf[0]);
             else mfma32_acc(acc[mt], vf[r][0], pf[0]);
             mfma32_acc(acc[mt], vf[r][1], pf[1]);
         }
@@ -454,7 +341,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_bf16_kernel(DecodePara
     if (bad_block && threadIdx.x == 0) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
 
     // ---- finalise: O = acc / l, LSE = ln 2 * (m + log2 l) --------------------
-    const bool empty = !(l > 0.f);
+    const bool empty = l == 0.f;  // NaN stays visible
     const float inv = empty ? 0.f : 1.f / l;
     const float lse = empty ? -INFINITY : (m + log2f(l)) * 0.6931471805599453f;
     const size_t hrow = size_t(id.row) * p.H + head;

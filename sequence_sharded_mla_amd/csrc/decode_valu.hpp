@@ -218,7 +218,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams p) {
 
     // finalise: O = acc / l, LSE = m + log l; an empty row is (0, -inf)
     const int h = tid >> 4, tl = tid & 15;
-    const bool empty = !(l > 0.f);
+    const bool empty = l == 0.f;  // NaN stays visible
     const float inv = empty ? 0.f : 1.f / l;
     const float lse = empty ? -INFINITY : m + logf(l);
     const size_t head = size_t(id.row) * p.H + h0 + h;

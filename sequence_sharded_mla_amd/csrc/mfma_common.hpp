@@ -1,0 +1,163 @@
+// Helpers shared by the matrix-core decode kernels (gfx950): operand types,
+// inline-asm MFMA forms with explicit accumulator placement, direct
+// global->LDS loads, explicit vmcnt waits, cross-half reductions.
+#pragma once
+
+#include "common.hpp"
+
+namespace mla {
+namespace mfma {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr int kSub = 32;                   // tokens per sub-tile
+constexpr int kDvTiles = kLatent / 32;     // 16 32-dim tiles of the output
+constexpr int kQLatSteps = kLatent / 16;   // 32 K-steps over the latent dims
+
+// vmcnt-only wait (expcnt / lgkmcnt left at their maxima), gfx9 encoding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Score-product MFMAs with the accumulator in VGPRs.  The output
+// accumulators fill the AGPR file, and the compiler would otherwise place
+// this accumulator there too and shuttle output tiles through VGPRs.
+// Back-to-back accumulation into the same registers needs no wait states;
+// the last MFMA of a chain is followed by enough NOPs for a VALU read of the
+// result (an 8-pass XDL write needs 11).
+//
+// FRESH = an A or B operand may have been written by a VALU instruction
+// right before (e.g. fp8 codes widened in registers).  The hardware does not
+// interlock a VALU write against a following MFMA read of the same VGPR (two
+// wait states are required); the compiler pads its own MFMAs but cannot see
+// into asm, so these forms lead with three NOP cycles.
+template <bool FRESH = false>
+__device__ __forceinline__ void mfma32_v_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    if constexpr (FRESH)
+        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+template <bool FRESH = false>
+__device__ __forceinline__ void mfma32_v(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    if constexpr (FRESH)
+        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+template <bool FRESH = false>
+__device__ __forceinline__ void mfma32_v_last(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    if constexpr (FRESH)
+        asm volatile(
+            "s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+            "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+            : "+v"(c)
+            : "v"(a), "v"(b));
+    else
+        asm volatile(
+            "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+            "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+            : "+v"(c)
+            : "v"(a), "v"(b));
+}
+
+// Output-product MFMA with the accumulator pinned to AGPRs.  Issued as
+// inline asm so the whole 256-register output accumulator stays in the AGPR
+// file.  FRESH as above (operands converted in registers just before).
+template <bool FRESH = false>
+__device__ __forceinline__ void mfma32_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    if constexpr (FRESH)
+        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// Wait states after the last asm MFMA writes before ordinary code reads the
+// accumulators (the compiler does not see the asm as an MFMA).
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+
+// max / sum of x over lanes i and i ^ 32 (one cross-half VALU swap)
+__device__ __forceinline__ float xhalf_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One wave-wide direct-to-LDS load: lane i copies 16 bytes from
+// gbase + voff(i) (gbase uniform, in SGPRs) to LDS byte lds_base + 16 i.  Issued as inline asm so the
+// compiler does not see an LDS write in flight: it would otherwise wait for
+// every outstanding load (vmcnt 0) before each LDS transpose read.  The
+// waits that order these loads before their LDS readers are explicit
+// (wait_vm + barrier).  M0 holds the LDS base; writing M0 needs one wait
+// state before the load.
+__device__ __forceinline__ void dma16(const void* gbase, int voff, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(gbase), "s"(lds_base)
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((const MLA_LDS void*)p));
+}
+
+// Same load with a 64-bit per-lane global address (gathered rows).
+__device__ __forceinline__ void dma16_v(const void* gptr, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(gptr), "s"(lds_base)
+        : "memory", "m0");
+}
+
+// A finite, all-zero row: the load source for sub-tiles whose block id is
+// invalid (their scores are masked; zeros keep 0 * value finite).
+__device__ const __attribute__((aligned(16))) uint8_t kZeroRow[1152] = {};
+
+// acc *= a for one 16-register accumulator tile held in AGPRs.  Written as
+// register moves + a multiply so the accumulators never leave the AGPR file.
+__device__ __forceinline__ void scale_acc(f32x16& acc, float a) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        float x = acc[e];
+        float tmp;
+        asm volatile(
+            "v_accvgpr_read_b32 %1, %0\n\t"
+            "v_mul_f32 %1, %1, %2\n\t"
+            "v_accvgpr_write_b32 %0, %1"
+            : "+a"(x), "=&v"(tmp)
+            : "v"(a));
+        acc[e] = x;
+    }
+}
+
+// Growth of a head's running max (log2 units) tolerated before the
+// accumulators are rescaled: probabilities are formed against a reference
+// max that may lag the true running max by at most this much, so they stay
+// below 2^kLag; O and the normaliser share the reference, so the result is
+// unchanged.
+constexpr float kLag = 8.f;
+
+}  // namespace mfma
+}  // namespace mla

@@ -268,3 +268,42 @@ def test_bad_block_id_is_skipped(heads):
         o_ref, l_ref = attention.attend(q[b, 0], k, lat, sp.scale)
         assert np.abs(o_sh[s, b] - o_ref).max() <= TOL_O
         assert np.abs(l_sh[s, b] - l_ref).max() <= TOL_LSE
+
+
+@pytest.mark.parametrize("topk", [0, 300])
+def test_fp8_128_heads(topk):
+    if topk:
+        sp = S["sparse_fp8_topk2048"].with_(batch=2, heads=128, context=4000, topk=topk, seed=20)
+    else:
+        sp = S["dense_fp8_mixed"].with_(batch=3, heads=128, ctx_range=(50, 5000), seed=21)
+    x = workload.generate(sp)
+    _, step = run_gpu(x)
+    compare(x, step)
+
+
+def test_sparse_topk_beyond_lds_list():
+    # more top-K entries than the matrix-core path keeps in LDS
+    sp = S["sparse_fp8_topk2048"].with_(batch=1, context=40000, topk=2500, seed=22)
+    x = workload.generate(sp)
+    _, step = run_gpu(x)
+    compare(x, step)
+
+
+def test_fp8_zero_scale_groups_and_bad_block():
+    sp = S["dense_fp8_mixed"].with_(batch=2, ctx_range=(3000, 3000), seed=23)
+    x = workload.generate(sp)
+    x.scales[:50, 1] = 0.0          # a whole group of some rows scaled to zero
+    cache = layout.pack(x, device="cuda")
+    bt = cache.block_tables.clone()
+    bt[1, 1, 2] = -1                 # shard 1, request 1, local block 2
+    cache.block_tables = bt
+    step = ShardedDecodeStep(cache, sp.out_dtype)
+    step()
+    torch.cuda.synchronize()
+    assert mla_get_device_error(step.workspace) & MLA_DEVERR_BLOCK_TABLE
+    o_sh = to_np(step.o_partials).reshape(sp.n_shards, 2, sp.heads, 512)
+    assert np.isfinite(o_sh).all()
+    # shard 0 is untouched by the bad block: compare it with the oracle
+    from gpu_cases import oracle_for, max_err
+    ref = oracle_for(x, full=False)
+    assert max_err(o_sh[0], ref["o_shards"][0][:, 0]) <= TOL_O
