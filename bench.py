@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "dense_bf16_32k"
 METRIC = "MLA decode attention: achieved HBM GB/s (% of peak) and KV tokens/s at 32K"
-KERNEL_SOURCES = ["decode_valu.hpp", "decode_mfma.hpp", "common.hpp", "params.hpp", "api.hip",
+KERNEL_SOURCES = ["decode_valu.hpp", "decode_mfma.hpp", "decode_fp8.hpp", "mfma_common.hpp", "common.hpp",
+                  "params.hpp", "api.hip",
                   "reduce.hpp", "plan.hpp", "host.cpp"]
 
 
