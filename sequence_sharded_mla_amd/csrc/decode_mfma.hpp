@@ -16,7 +16,7 @@
 // A operand (16 B per lane); V^T is read with ds_read_b64_tr_b16, which
 // transposes 4 x 4 16-bit blocks across a 16-lane group, so each lane gets
 // four consecutive tokens of one latent dimension.  Rows are stored with
-// their 16-byte chunks XOR-swizzled by a 3-bit function of the row so that
+// their 16-byte chunks XOR-swizzled by a 4-bit function of the row so that
 // both read patterns hit every LDS bank once per pass.
 //
 // Scores use exact bf16 products with float32 accumulation; probabilities

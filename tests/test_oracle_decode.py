@@ -106,3 +106,58 @@ def test_sparse_row_with_no_valid_index():
     r = decode.mla_decode(q, rows, np.array([10]), 1, 2, SCALE, topk_idx=idx)
     assert np.all(r["o"] == 0) and np.all(np.isneginf(r["lse"]))
     assert np.all(r["o_shards"] == 0) and np.all(np.isneginf(r["lse_shards"]))
+
+
+def test_brute_force_scalar_loops():
+    """Pure-Python scalar loops on tiny inputs: every shard's partial and the
+    merged result, written out term by term with math.exp / math.log."""
+    import math
+    rng = np.random.default_rng(8)
+    B, Tq, H, N = 2, 2, 2, 3
+    lens = [7, 12]
+    q, store, rows = _make(rng, B, Tq, H, lens)
+    r = decode.mla_decode(q, rows, np.array(lens), Tq, N, SCALE)
+    for b in range(B):
+        L = lens[b]
+        for t in range(Tq):
+            last = L - Tq + t
+            for h in range(H):
+                qv = [float(v) for v in q[b, t, h]]
+                parts = []
+                for s in range(N):
+                    sc = {}
+                    for p in range(last + 1):
+                        if p % N != s:
+                            continue
+                        kv = store[b][p]
+                        dot = 0.0
+                        for d in range(576):
+                            dot += qv[d] * float(kv[d])
+                        sc[p] = SCALE * dot
+                    if not sc:
+                        parts.append((None, -math.inf))
+                        o_ref, l_ref = [0.0] * 512, -math.inf
+                    else:
+                        mx = max(sc.values())
+                        den = sum(math.exp(v - mx) for v in sc.values())
+                        l_ref = mx + math.log(den)
+                        o_ref = [0.0] * 512
+                        for p, v in sc.items():
+                            w = math.exp(v - l_ref)
+                            for d in range(512):
+                                o_ref[d] += w * float(store[b][p][d])
+                        parts.append((o_ref, l_ref))
+                    assert abs(r["lse_shards"][s, b, t, h] - l_ref) < 1e-12 or (
+                        l_ref == -math.inf and r["lse_shards"][s, b, t, h] == -np.inf)
+                    assert np.allclose(r["o_shards"][s, b, t, h], o_ref, atol=1e-12)
+                m = max(l for _, l in parts)
+                wsum = sum(math.exp(l - m) for _, l in parts if l > -math.inf)
+                o_m = [0.0] * 512
+                for o, l in parts:
+                    if o is None:
+                        continue
+                    w = math.exp(l - m) / wsum
+                    for d in range(512):
+                        o_m[d] += w * o[d]
+                assert abs(r["lse"][b, t, h] - (m + math.log(wsum))) < 1e-12
+                assert np.allclose(r["o"][b, t, h], o_m, atol=1e-12)
