@@ -74,7 +74,7 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     const bool mfma_fp8 = d->kv_dtype == MLA_FP8_DS && (d->num_heads == 64 || d->num_heads == 128) &&
                           d->topk <= mfma::kMaxTopk;
     if (mfma_bf16) {
-        hipLaunchKernelGGL(mfma::decode_mfma_bf16_kernel<4>, dim3(n_items), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(mfma::decode_mfma_bf16_kernel, dim3(n_items), dim3(256), 0, s, p);
     } else if (mfma_fp8) {
         const bool sparse = d->topk > 0;
         if (d->num_heads == 64) {

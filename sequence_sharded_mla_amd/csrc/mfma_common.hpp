@@ -3,6 +3,8 @@
 // global->LDS loads, explicit vmcnt waits, cross-half reductions.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace mla {
@@ -114,6 +116,28 @@ __device__ __forceinline__ void dma16(const void* gbase, int voff, uint32_t lds_
         :
         : "v"(voff), "s"(gbase), "s"(lds_base)
         : "memory", "m0");
+}
+
+// f(integral_constant<int, K>) for K = K0 .. K1 - 1, unrolled at compile time
+template <int K0, int K1, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (K0 < K1) {
+        f(std::integral_constant<int, K0>{});
+        static_for<K0 + 1, K1>(f);
+    }
+}
+
+// The same load with the LDS base given as a uniform register plus a
+// compile-time byte offset, summed straight into M0.
+template <int IMM>
+__device__ __forceinline__ void dma16_at(const void* gbase, int voff, uint32_t lds_base) {
+    asm volatile(
+        "s_add_u32 m0, %2, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(gbase), "s"(lds_base), "n"(IMM)
+        : "memory", "m0", "scc");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
