@@ -44,18 +44,18 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // right before (e.g. fp8 codes widened in registers).  The hardware does not
 // interlock a VALU write against a following MFMA read of the same VGPR (two
 // wait states are required); the compiler pads its own MFMAs but cannot see
-// into asm, so these forms lead with three NOP cycles.
+// into asm, so these forms lead with two NOP cycles.
 template <bool FRESH = false>
 __device__ __forceinline__ void mfma32_v_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
     if constexpr (FRESH)
-        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
     else
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
 }
 template <bool FRESH = false>
 __device__ __forceinline__ void mfma32_v(f32x16& c, const bf16x8& a, const bf16x8& b) {
     if constexpr (FRESH)
-        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
     else
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
@@ -63,7 +63,7 @@ template <bool FRESH = false>
 __device__ __forceinline__ void mfma32_v_last(f32x16& c, const bf16x8& a, const bf16x8& b) {
     if constexpr (FRESH)
         asm volatile(
-            "s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+            "s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
             "s_nop 7\n\ts_nop 7\n\ts_nop 7"
             : "+v"(c)
             : "v"(a), "v"(b));
@@ -81,10 +81,16 @@ __device__ __forceinline__ void mfma32_v_last(f32x16& c, const bf16x8& a, const 
 template <bool FRESH = false>
 __device__ __forceinline__ void mfma32_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
     if constexpr (FRESH)
-        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     else
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
+// Wait states between an asm MFMA chain into c and the first VALU read of
+// c.  c is a tied operand, so the compiler cannot move a reader above it.
+__device__ __forceinline__ void mfma_result_wait(f32x16& c) {
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(c));
+}
+
 // Wait states after the last asm MFMA writes before ordinary code reads the
 // accumulators (the compiler does not see the asm as an MFMA).
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
@@ -137,6 +143,19 @@ __device__ __forceinline__ void dma16_at(const void* gbase, int voff, uint32_t l
         "global_load_lds_dwordx4 %0, %1"
         :
         : "v"(voff), "s"(gbase), "s"(lds_base), "n"(IMM)
+        : "memory", "m0", "scc");
+}
+
+// Per-lane 64-bit global address, LDS base in a register plus a
+// compile-time offset.
+template <int IMM>
+__device__ __forceinline__ void dma16_v_at(const void* gptr, uint32_t lds_base) {
+    asm volatile(
+        "s_add_u32 m0, %1, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(gptr), "s"(lds_base), "n"(IMM)
         : "memory", "m0", "scc");
 }
 
