@@ -104,7 +104,7 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     }
     if ((st = launch_status()) != MLA_OK) return st;
     if (plan.n_chunks > 1) {
-        hipLaunchKernelGGL(chunk_combine_kernel, dim3(uint32_t(plan.rows), uint32_t(d->num_heads / 2)),
+        hipLaunchKernelGGL(chunk_combine_kernel, dim3(uint32_t(plan.rows), uint32_t(d->num_heads / 4)),
                            dim3(256), 0, s, p);
         if ((st = launch_status()) != MLA_OK) return st;
     }
@@ -156,7 +156,7 @@ int32_t mla_lse_merge(int32_t n_parts, int64_t rows, int32_t dv, int32_t part_dt
         return MLA_ERR_ALIGN;
     if (rows == 0) return MLA_OK;
     if (rows > (int64_t(1) << 31)) return MLA_ERR_SHAPE;
-    const dim3 grid(uint32_t((rows + 1) / 2));
+    const dim3 grid(uint32_t((rows + 3) / 4));
     hipStream_t s = mla::as_stream(stream);
     if (part_dtype == MLA_F32)
         hipLaunchKernelGGL(mla::lse_merge_kernel<float>, grid, dim3(256), 0, s, n_parts, rows,

@@ -307,3 +307,14 @@ def test_fp8_zero_scale_groups_and_bad_block():
     from gpu_cases import oracle_for, max_err
     ref = oracle_for(x, full=False)
     assert max_err(o_sh[0], ref["o_shards"][0][:, 0]) <= TOL_O
+
+
+def test_chunk_combine_more_than_64_chunks():
+    # one shard holding 266K tokens: the row splits into more than 64 chunks,
+    # so the combine runs its weights in two groups of parts
+    sp = S["long_fp8_1m"].with_(batch=1, n_shards=1, context=65 * 4096 + 100, seed=12)
+    x = workload.generate(sp)
+    cache, step = run_gpu(x)
+    rows = sp.batch * sp.q_len
+    assert step.workspace.numel() > 64 * rows * sp.heads * 512 * 4, "expected > 64 chunks"
+    compare(x, step)
