@@ -48,10 +48,12 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     p.lse_out = lse;
     uint8_t* w = static_cast<uint8_t*>(ws);
     p.err = reinterpret_cast<uint32_t*>(w);
-    if (plan.n_chunks > 1) {
-        p.ws_o = reinterpret_cast<float*>(w + plan.ws_o_off);
+    p.plan_hdr = reinterpret_cast<const int32_t*>(w);
+    if (plan.planned) {
+        p.items = reinterpret_cast<const int32_t*>(w + plan.items_off);
+        p.row_info = reinterpret_cast<const int32_t*>(w + plan.row_info_off);
+        p.ws_o = w + plan.ws_o_off;
         p.ws_lse = reinterpret_cast<float*>(w + plan.ws_lse_off);
-        p.ws_cnt = reinterpret_cast<uint32_t*>(w + plan.ws_cnt_off);
     }
     p.pool_blocks = d->pool_blocks;
     p.row_bytes = int32_t(row_bytes(d->kv_dtype));
@@ -63,13 +65,18 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     p.shard_begin = shard_begin;
     p.shard_count = shard_count;
     p.n_shards = n_shards;
-    p.n_chunks = plan.n_chunks;
-    p.tiles_per_chunk = plan.tiles_per_chunk;
+    p.rows = plan.rows;
     p.out_dtype = d->out_dtype;
     p.scale = d->softmax_scale;
 
     hipStream_t s = as_stream(stream);
-    const uint32_t n_items = uint32_t(plan.rows) * plan.n_chunks;
+    if (plan.planned) {
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, p, plan.target,
+                           reinterpret_cast<int32_t*>(w), reinterpret_cast<int32_t*>(w + plan.items_off),
+                           reinterpret_cast<int32_t*>(w + plan.row_info_off));
+        if ((st = launch_status()) != MLA_OK) return st;
+    }
+    const uint32_t n_items = uint32_t(plan.items_max);
     const bool mfma_bf16 = d->kv_dtype == MLA_BF16 && d->topk == 0 && d->num_heads == 128;
     const bool mfma_fp8 = d->kv_dtype == MLA_FP8_DS && (d->num_heads == 64 || d->num_heads == 128) &&
                           d->topk <= mfma::kMaxTopk;
@@ -103,7 +110,7 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
         }
     }
     if ((st = launch_status()) != MLA_OK) return st;
-    if (plan.n_chunks > 1) {
+    if (plan.planned) {
         hipLaunchKernelGGL(chunk_combine_kernel, dim3(uint32_t(plan.rows), uint32_t(d->num_heads / 4)),
                            dim3(256), 0, s, p);
         if ((st = launch_status()) != MLA_OK) return st;

@@ -97,7 +97,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     constexpr int kRopeLoads = kSub / 8 / NW;   // rope loads per wave (8 rows each)
     constexpr int kSclRows = kSub / NW;         // scale rows per wave (one load)
     constexpr int kLoads = kCodeLoads + kRopeLoads + 1;
-    const RowId id = decode_row(p, blockIdx.x);
+    RowId id;
+    if (!work_item(p, blockIdx.x, id)) return;  // past the last planned item
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -121,8 +122,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
             if (threadIdx.x == 0) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
             local = p.max_blocks * kBlock;
         }
-        tok0 = id.chunk * p.tiles_per_chunk * kBlock;
-        tok1 = min(tok0 + p.tiles_per_chunk * kBlock, local);
+        tok0 = id.chunk * id.chunk_tok;
+        tok1 = id.chunk_tok ? min(tok0 + id.chunk_tok, local) : local;
         if (tok1 < tok0) tok1 = tok0;
     } else {
         // compact the entries this shard owns, in entry order
@@ -471,11 +472,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     const bool empty = l == 0.f;  // NaN stays visible
     const float inv = empty ? 0.f : 1.f / l;
     const float lse = empty ? -INFINITY : (m + log2f(l)) * 0.6931471805599453f;
-    const size_t hrow = size_t(id.row) * p.H + head;
-    const bool direct = p.n_chunks == 1;
-    const size_t slot = (size_t(id.row) * p.n_chunks + id.chunk) * p.H + head;
-    if (direct && p.out_dtype == MLA_BF16) {
-        uint16_t* o = static_cast<uint16_t*>(p.o_out) + hrow * kLatent;
+    // whole row: the shard's output; a chunk of a split row: its partial slot
+    const bool direct = id.slot < 0;
+    const size_t orow = direct ? size_t(id.row) * p.H + head : size_t(id.slot) * p.H + head;
+    if (p.out_dtype == MLA_BF16) {
+        uint16_t* o = static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) + orow * kLatent;
 #pragma unroll
         for (int mt = 0; mt < kDvTiles; ++mt)
 #pragma unroll
@@ -489,7 +490,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
                 *reinterpret_cast<uint2*>(o + d) = w;
             }
     } else {
-        float* o = direct ? static_cast<float*>(p.o_out) + hrow * kLatent : p.ws_o + slot * kLatent;
+        float* o = static_cast<float*>(direct ? p.o_out : p.ws_o) + orow * kLatent;
 #pragma unroll
         for (int mt = 0; mt < kDvTiles; ++mt)
 #pragma unroll
@@ -500,10 +501,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
                                 acc[mt][4 * q4 + 2] * inv, acc[mt][4 * q4 + 3] * inv);
             }
     }
-    if (half == 0) {
-        if (direct) p.lse_out[hrow] = lse;
-        else p.ws_lse[slot] = lse;
-    }
+    if (half == 0) (direct ? p.lse_out : p.ws_lse)[orow] = lse;
 }
 
 }  // namespace mfma

@@ -72,7 +72,8 @@ struct alignas(16) SmemBf16 {
 
 __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p) {
     __shared__ SmemBf16 sm;
-    const RowId id = decode_row(p, blockIdx.x);
+    RowId id;
+    if (!work_item(p, blockIdx.x, id)) return;  // past the last planned item
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int half = lane >> 5;
@@ -90,8 +91,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         if (threadIdx.x == 0) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
         local = p.max_blocks * kBlock;
     }
-    const int32_t tok0 = id.chunk * p.tiles_per_chunk * kBlock;
-    int32_t tok1 = tok0 + p.tiles_per_chunk * kBlock;
+    const int32_t tok0 = id.chunk * id.chunk_tok;
+    int32_t tok1 = id.chunk_tok ? tok0 + id.chunk_tok : local;
     if (tok1 > local) tok1 = local;
     const int n_sub = tok1 > tok0 ? (tok1 - tok0 + kSub - 1) / kSub : 0;
     // the pipelined loop below is unrolled by the ring size and always runs
@@ -432,11 +433,11 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     const bool empty = l == 0.f;  // NaN stays visible
     const float inv = empty ? 0.f : 1.f / l;
     const float lse = empty ? -INFINITY : (m + log2f(l)) * 0.6931471805599453f;
-    const size_t hrow = size_t(id.row) * p.H + head;
-    const bool direct = p.n_chunks == 1;
-    const size_t slot = (size_t(id.row) * p.n_chunks + id.chunk) * p.H + head;
-    if (direct && p.out_dtype == MLA_BF16) {
-        uint16_t* o = static_cast<uint16_t*>(p.o_out) + hrow * kLatent;
+    // whole row: the shard's output; a chunk of a split row: its partial slot
+    const bool direct = id.slot < 0;
+    const size_t orow = direct ? size_t(id.row) * p.H + head : size_t(id.slot) * p.H + head;
+    if (p.out_dtype == MLA_BF16) {
+        uint16_t* o = static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) + orow * kLatent;
 #pragma unroll
         for (int mt = 0; mt < kDvTiles; ++mt)
 #pragma unroll
@@ -450,7 +451,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
                 *reinterpret_cast<uint2*>(o + d) = w;
             }
     } else {
-        float* o = direct ? static_cast<float*>(p.o_out) + hrow * kLatent : p.ws_o + slot * kLatent;
+        float* o = static_cast<float*>(direct ? p.o_out : p.ws_o) + orow * kLatent;
 #pragma unroll
         for (int mt = 0; mt < kDvTiles; ++mt)
 #pragma unroll
@@ -461,10 +462,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
                                 acc[mt][4 * q4 + 2] * inv, acc[mt][4 * q4 + 3] * inv);
             }
     }
-    if (half == 0) {
-        if (direct) p.lse_out[hrow] = lse;
-        else p.ws_lse[slot] = lse;
-    }
+    if (half == 0) (direct ? p.lse_out : p.ws_lse)[orow] = lse;
 }
 
 }  // namespace mfma

@@ -108,7 +108,8 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, Smem& sm, int c
 template <int KV>
 __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams p) {
     __shared__ Smem sm;
-    const RowId id = decode_row(p, blockIdx.x);
+    RowId id;
+    if (!work_item(p, blockIdx.x, id)) return;  // past the last planned item
     const int h0 = blockIdx.y * kHeads;
     const int tid = threadIdx.x;
     const int s = p.shard_begin + id.s_rel;
@@ -141,8 +142,8 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams p) {
             if (tid == 0) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
             local = p.max_blocks * kBlock;
         }
-        const int32_t tok0 = id.chunk * p.tiles_per_chunk * kBlock;
-        int32_t tok1 = tok0 + p.tiles_per_chunk * kBlock;
+        const int32_t tok0 = id.chunk * id.chunk_tok;
+        int32_t tok1 = id.chunk_tok ? tok0 + id.chunk_tok : local;
         if (tok1 > local) tok1 = local;
         for (int32_t j0 = tok0; j0 < tok1; j0 += kTile) {
             const int cnt = min(kTile, tok1 - j0);
@@ -221,25 +222,19 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams p) {
     const bool empty = l == 0.f;  // NaN stays visible
     const float inv = empty ? 0.f : 1.f / l;
     const float lse = empty ? -INFINITY : m + logf(l);
-    const size_t head = size_t(id.row) * p.H + h0 + h;
-    if (p.n_chunks == 1) {
-        if (p.out_dtype == MLA_F32) {
-            float* o = static_cast<float*>(p.o_out) + head * kLatent;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) o[tl + 16 * i] = acc[i] * inv;
-        } else {
-            uint16_t* o = static_cast<uint16_t*>(p.o_out) + head * kLatent;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) o[tl + 16 * i] = f32_to_bf16(acc[i] * inv);
-        }
-        if (tl == 0) p.lse_out[head] = lse;
-    } else {
-        const size_t slot = (size_t(id.row) * p.n_chunks + id.chunk) * p.H + h0 + h;
-        float* o = p.ws_o + slot * kLatent;
+    // whole row: the shard's output; a chunk of a split row: its partial slot
+    const bool direct = id.slot < 0;
+    const size_t head = (direct ? size_t(id.row) : size_t(id.slot)) * p.H + h0 + h;
+    if (p.out_dtype == MLA_F32) {
+        float* o = static_cast<float*>(direct ? p.o_out : p.ws_o) + head * kLatent;
 #pragma unroll
         for (int i = 0; i < 32; ++i) o[tl + 16 * i] = acc[i] * inv;
-        if (tl == 0) p.ws_lse[slot] = lse;
+    } else {
+        uint16_t* o = static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) + head * kLatent;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) o[tl + 16 * i] = f32_to_bf16(acc[i] * inv);
     }
+    if (tl == 0) (direct ? p.lse_out : p.ws_lse)[head] = lse;
 }
 
 }  // namespace valu

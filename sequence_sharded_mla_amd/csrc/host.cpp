@@ -45,36 +45,47 @@ int32_t validate_desc(const mla_decode_desc* d) {
 
 static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// Items the device plan aims for: about two per workgroup that fits on the
+// chip at once (256 compute units; the fp8 kernel for 64 heads fits two
+// workgroups per unit).
+static int32_t plan_target(const mla_decode_desc* d) {
+    if (d->kv_dtype == MLA_FP8_DS && d->num_heads == 64) return 1024;
+    if (d->kv_dtype == MLA_F32 || (d->kv_dtype == MLA_BF16 && d->num_heads != 128)) return 1024;
+    return 512;
+}
+
 int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan) {
     int32_t st = validate_desc(d);
     if (st != MLA_OK) return st;
     if (shard_count < 1 || shard_count > 4096) return MLA_ERR_SHARD;
     Plan p;
     p.rows = int32_t(int64_t(shard_count) * d->batch * d->q_len);
-    if (d->topk > 0) {
-        p.n_chunks = 1;
-        p.tiles_per_chunk = 0;
-    } else {
-        // Chunk so the launch carries on the order of a thousand chunks, but
-        // never fewer than 64 tiles (4096 local tokens) per chunk: a chunk
-        // partial costs H * 513 floats written and read again, which must
-        // stay small next to the chunk's cache bytes.
-        const int64_t total_tiles = int64_t(p.rows) * d->max_blocks;
-        int64_t tpc = (total_tiles + 1023) / 1024;
-        if (tpc < 64) tpc = 64;
-        if (tpc > d->max_blocks) tpc = d->max_blocks;
-        p.tiles_per_chunk = int32_t(tpc);
-        p.n_chunks = int32_t((d->max_blocks + tpc - 1) / tpc);
-    }
+    // a row holds at most max_blocks * 64 local tokens; when that fits in one
+    // chunk of the smallest size, every row is one item and no plan is needed
+    p.planned = d->topk == 0 && int64_t(d->max_blocks) * kBlock > kChunkMin;
+    p.items_max = p.rows;
     int64_t off = kWsHeader;
-    if (p.n_chunks > 1) {
-        const int64_t slots = int64_t(p.rows) * p.n_chunks * d->num_heads;
+    if (p.planned) {
+        p.target = plan_target(d);
+        // items per row <= local / chunk + 1 and sum(local) / chunk <= target
+        p.items_max = p.rows + p.target;
+        // a row splits only when local > chunk >= kChunkMin, into at most
+        // 2 local / chunk items: at most 2 target and 2 total / kChunkMin
+        const int64_t total_bound = int64_t(p.rows) * d->max_blocks * kBlock;
+        int64_t slots = 2 * int64_t(p.target);
+        const int64_t by_len = 2 * ((total_bound + kChunkMin - 1) / kChunkMin);
+        if (by_len < slots) slots = by_len;
+        if (p.items_max < slots) slots = p.items_max;
+        p.slots = int32_t(slots);
+        const int64_t out_bytes = d->out_dtype == MLA_F32 ? 4 : 2;
+        p.items_off = off;
+        off = align_up(off + int64_t(p.items_max) * 16, 256);
+        p.row_info_off = off;
+        off = align_up(off + int64_t(p.rows) * 8, 256);
         p.ws_o_off = off;
-        off = align_up(off + slots * kLatent * 4, 256);
+        off = align_up(off + slots * d->num_heads * kLatent * out_bytes, 256);
         p.ws_lse_off = off;
-        off = align_up(off + slots * 4, 256);
-        p.ws_cnt_off = off;
-        off = align_up(off + int64_t(p.rows) * 4, 256);
+        off = align_up(off + slots * d->num_heads * 4, 256);
     }
     p.ws_bytes = off;
     *plan = p;

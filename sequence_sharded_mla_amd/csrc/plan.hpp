@@ -1,12 +1,14 @@
-// Host-side validation and work planning for one decode step.
+// Host-side validation and workspace sizing for one decode step.
 //
 // Pure C++ (no HIP): the same code is compiled into the library and can be
-// exercised without a GPU.  A plan splits every (shard, request, query token)
-// row of a dense decode into `n_chunks` chunks of `tiles_per_chunk` 64-token
-// tiles of that shard's local cache; each chunk is one workgroup.  When a row
-// has more than one chunk, the chunks write float32 (O, LSE) partials into the
-// workspace and a combine pass merges them with the same LSE rule as the
-// cross-shard merge.
+// exercised without a GPU.  Sparse steps run one workgroup per (shard,
+// request, query token) row.  Dense steps whose rows may exceed one chunk
+// are planned on the device: a plan kernel reads the real context lengths,
+// picks a chunk size from the total work (about two chunks per resident
+// workgroup, never fewer than kChunkMin tokens), and lists (row, chunk)
+// items; rows of one chunk write their result directly, split rows write
+// partials into the workspace and a combine pass merges them with the same
+// LSE rule as the cross-shard merge.
 #pragma once
 
 #include <cstdint>
@@ -20,16 +22,21 @@ constexpr int kRope = 64;
 constexpr int kDk = kLatent + kRope;
 constexpr int kBlock = 64;
 constexpr int kFp8Group = 128;
-constexpr int64_t kWsHeader = 256;  // device error word + reserved
+constexpr int64_t kWsHeader = 256;  // int32 [0] device error word, [1] item count, [2] chunk tokens
+
+constexpr int32_t kChunkMin = 4096;  // fewest local tokens per chunk of a split row
 
 struct Plan {
-    int32_t rows = 0;             // shard_count * B * Tq
-    int32_t n_chunks = 1;         // chunks per row
-    int32_t tiles_per_chunk = 0;  // 64-token tiles per chunk (dense)
+    int32_t rows = 0;           // shard_count * B * Tq
+    bool planned = false;       // dense rows that may split: device plan + combine
+    int32_t target = 0;         // items the device plan aims for
+    int32_t items_max = 0;      // workgroups to launch (an upper bound on items)
+    int32_t slots = 0;          // partial slots of split rows
     int64_t ws_bytes = kWsHeader; // workspace the call needs
-    int64_t ws_o_off = 0;         // float [rows][n_chunks][H][512]
-    int64_t ws_lse_off = 0;       // float [rows][n_chunks][H]
-    int64_t ws_cnt_off = 0;       // uint32 [rows] completion counters
+    int64_t items_off = 0;      // int32 [items_max][4]
+    int64_t row_info_off = 0;   // int32 [rows][2]
+    int64_t ws_o_off = 0;       // out dtype [slots][H][512]
+    int64_t ws_lse_off = 0;     // float [slots][H]
 };
 
 int64_t row_bytes(int32_t kv_dtype);

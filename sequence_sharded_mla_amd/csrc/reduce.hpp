@@ -110,16 +110,166 @@ __device__ __forceinline__ void merge_wave(int n, const T* o, size_t part_stride
     if (lse_out && lane == 0) lse_out[0] = (M == -INFINITY) ? -INFINITY : M + logf(W);
 }
 
-// Chunk partials of each (shard, request, query token) row -> that shard's
-// O_partial / LSE.  grid = (rows, H / 4), 256 threads = 4 heads.
+// Partials of split rows -> that shard's O_partial / LSE.  grid = (rows,
+// H / 4), 256 threads = 4 heads; rows of one item were written directly.
 __global__ void __launch_bounds__(256) chunk_combine_kernel(DecodeParams p) {
     const int row = blockIdx.x;
+    const int32_t slot0 = p.row_info[2 * size_t(row)];  // a row's slots are consecutive
+    const int32_t k = p.row_info[2 * size_t(row) + 1];
+    if (k <= 1) return;
     const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-    const size_t slot0 = size_t(row) * p.n_chunks * p.H + h;
     const size_t head = size_t(row) * p.H + h;
-    merge_wave<float>(p.n_chunks, p.ws_o + slot0 * kLatent, size_t(p.H) * kLatent,
-                      p.ws_lse + slot0, size_t(p.H), p.o_out, p.out_dtype, head * kLatent,
-                      p.lse_out + head, threadIdx.x & 63);
+    const size_t s0 = size_t(slot0) * p.H + h;
+    if (p.out_dtype == MLA_F32)
+        merge_wave<float>(k, static_cast<const float*>(p.ws_o) + s0 * kLatent, size_t(p.H) * kLatent,
+                          p.ws_lse + s0, size_t(p.H), p.o_out, p.out_dtype, head * kLatent,
+                          p.lse_out + head, threadIdx.x & 63);
+    else
+        merge_wave<uint16_t>(k, static_cast<const uint16_t*>(p.ws_o) + s0 * kLatent,
+                             size_t(p.H) * kLatent, p.ws_lse + s0, size_t(p.H), p.o_out,
+                             p.out_dtype, head * kLatent, p.lse_out + head, threadIdx.x & 63);
+}
+
+// Inclusive prefix sum over one workgroup of 1024 threads (16 waves); every
+// thread must call it.
+__device__ __forceinline__ int32_t block_scan_1024(int32_t x, int32_t* wave_tot, int32_t& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    int32_t before = 0;
+    total = 0;
+    for (int w = 0; w < 16; ++w) {
+        const int32_t t = wave_tot[w];
+        if (w < wave) before += t;
+        total += t;
+    }
+    __syncthreads();
+    return x + before;
+}
+
+__device__ __forceinline__ int64_t block_sum_1024(int64_t x, int64_t* wave_tot) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    if ((threadIdx.x & 63) == 0) wave_tot[threadIdx.x >> 6] = x;
+    __syncthreads();
+    int64_t t = 0;
+    for (int w = 0; w < 16; ++w) t += wave_tot[w];
+    __syncthreads();
+    return t;
+}
+
+// Device plan of a dense step (one workgroup of 1024 threads).
+//
+// The chunk size T comes from the real total of local tokens (about
+// `target` items, never below kChunkMin).  Row r becomes floor(local / T)
+// full chunks plus one remainder chunk when local is not a multiple of T
+// (a row with no token still gets one item, which writes (0, -inf)).  Items
+// are listed longest first, so the dispatcher ends on short work: all full
+// chunks, then the remainder chunks in eight size classes, largest first.
+// row_info[r] = (first partial slot, items of the row); the slots of a split
+// row are consecutive and follow its chunk order.
+__global__ void __launch_bounds__(1024) plan_kernel(DecodeParams p, int32_t target,
+                                                    int32_t* hdr, int32_t* items,
+                                                    int32_t* row_info) {
+    constexpr int kBuckets = 8;
+    __shared__ int32_t wave_tot[16];
+    __shared__ int64_t wave_sum64[16];
+    const int tid = threadIdx.x;
+    const int64_t cap = int64_t(p.max_blocks) * kBlock;
+    auto local_of = [&](int32_t row) -> int32_t {
+        RowId r;
+        r.row = row;
+        split_row(p, r);
+        int32_t visible = p.context_lens[r.b] - p.Tq + r.t + 1;
+        if (visible < 0) visible = 0;
+        const int32_t local = dev_local_len(visible, p.shard_begin + r.s_rel, p.n_shards);
+        return local > cap ? int32_t(cap) : local;
+    };
+    int64_t tot = 0;
+    for (int32_t r = tid; r < p.rows; r += 1024) tot += local_of(r);
+    tot = block_sum_1024(tot, wave_sum64);
+    int64_t chunk = (tot + target - 1) / target;
+    chunk = (chunk + kBlock - 1) / kBlock * kBlock;
+    if (chunk < kChunkMin) chunk = kChunkMin;
+    if (chunk > (int64_t(1) << 30)) chunk = int64_t(1) << 30;
+    const int32_t T = int32_t(chunk);
+
+    // shape of row r: full chunks, remainder chunk (0/1), its size class
+    auto shape = [&](int32_t r, int32_t& full, int32_t& rem, int32_t& bucket) {
+        full = 0;
+        rem = 0;
+        bucket = -1;
+        if (r >= p.rows) return;
+        const int32_t local = local_of(r);
+        full = local / T;
+        const int32_t left = local - full * T;
+        if (left > 0 || local == 0) {
+            rem = 1;
+            bucket = int32_t(int64_t(left) * kBuckets / T);
+        }
+    };
+    // counts: full chunks, remainder chunks per size class
+    int64_t n_full = 0;
+    int64_t n_b[kBuckets] = {};
+    for (int32_t r0 = 0; r0 < p.rows; r0 += 1024) {
+        int32_t full, rem, bucket;
+        shape(r0 + tid, full, rem, bucket);
+        n_full += full;
+        if (rem) n_b[bucket] += 1;
+    }
+    n_full = block_sum_1024(n_full, wave_sum64);
+    int64_t off_b[kBuckets];
+    int64_t next = n_full;
+    for (int b = kBuckets - 1; b >= 0; --b) {
+        off_b[b] = next;
+        next += block_sum_1024(n_b[b], wave_sum64);
+    }
+    const int64_t n_items = next;
+
+    int64_t base_full = 0, base_split = 0;
+    int64_t base_b[kBuckets] = {};
+    for (int32_t r0 = 0; r0 < p.rows; r0 += 1024) {
+        const int32_t r = r0 + tid;
+        int32_t full, rem, bucket;
+        shape(r, full, rem, bucket);
+        const int32_t k = full + rem;
+        const int32_t ks = k > 1 ? k : 0;
+        int32_t sum_full, sum_ks;
+        const int32_t ex_full = block_scan_1024(full, wave_tot, sum_full) - full;
+        const int32_t ex_ks = block_scan_1024(ks, wave_tot, sum_ks) - ks;
+        int32_t ex_b = 0;
+        for (int b = 0; b < kBuckets; ++b) {
+            const int32_t in = bucket == b ? 1 : 0;
+            int32_t sum_b;
+            const int32_t ex = block_scan_1024(in, wave_tot, sum_b) - in;
+            if (in) ex_b = int32_t(off_b[b] + base_b[b] + ex);
+            base_b[b] += sum_b;
+        }
+        if (r < p.rows) {
+            const int64_t slot0 = k > 1 ? base_split + ex_ks : -1;
+            row_info[2 * size_t(r)] = int32_t(slot0);
+            row_info[2 * size_t(r) + 1] = k;
+            for (int32_t c = 0; c < k; ++c) {
+                const int64_t pos = c < full ? base_full + ex_full + c : ex_b;
+                int32_t* it = items + 4 * size_t(pos);
+                it[0] = r;
+                it[1] = c;
+                it[2] = k > 1 ? int32_t(slot0 + c) : -1;
+                it[3] = 0;
+            }
+        }
+        base_full += sum_full;
+        base_split += sum_ks;
+    }
+    if (tid == 0) {
+        hdr[1] = int32_t(n_items);
+        hdr[2] = T;
+    }
 }
 
 // Cross-part merge: grid = ceil(rows / 4), 256 threads = 4 rows.
