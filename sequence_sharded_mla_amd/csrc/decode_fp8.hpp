@@ -116,6 +116,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
 
     // ---- the tokens this workgroup attends ---------------------------------
     int32_t tok0 = 0, tok1 = 0;  // dense: local token range; sparse: list range
+    int total_owned = 0;
     if (!SPARSE) {
         int32_t local = dev_local_len(visible, s, p.n_shards);
         if ((local + kBlock - 1) / kBlock > p.max_blocks) {
@@ -126,38 +127,71 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         tok1 = id.chunk_tok ? min(tok0 + id.chunk_tok, local) : local;
         if (tok1 < tok0) tok1 = tok0;
     } else {
-        // compact the entries this shard owns, in entry order
+        // Compact the entries this shard owns, in entry order: wave w scans
+        // its own slice of the list (ballot + popcount, no barrier), then
+        // moves its owned entries down to their final position.
         const int32_t* idx = p.topk_idx + (size_t(id.b) * p.Tq + id.t) * p.topk;
-        int total = 0;
-        for (int32_t e0 = 0; e0 < p.topk; e0 += NW * 64) {
-            const int32_t e = e0 + threadIdx.x;
-            int32_t row = -1;
-            if (e < p.topk) {
-                const int32_t g = idx[e];
-                if (g >= 0) {
-                    if (g >= visible) {
-                        raise_error(p.err, MLA_DEVERR_INDEX);
-                    } else if (g % p.n_shards == s) {
-                        const int32_t j = g / p.n_shards;
-                        const int32_t blk = j / kBlock < p.max_blocks ? bt[j / kBlock] : -1;
-                        if (blk >= 0 && blk < p.pool_blocks) row = blk * kBlock + (j % kBlock);
-                        else raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
-                    }
-                }
-            }
-            const uint64_t mask = __ballot(row >= 0);
-            const int before = __popcll(mask & ((uint64_t(1) << lane) - 1));
-            if (lane == 0) sm.wave_cnt[wave] = __popcll(mask);
-            __syncthreads();
-            int base = total;
-            for (int w = 0; w < NW; ++w) {
-                if (w < wave) base += sm.wave_cnt[w];
-                total += sm.wave_cnt[w];
-            }
-            if (row >= 0) sm.rows[base + before] = row;
-            __syncthreads();
+        const int32_t slice = (p.topk + NW - 1) / NW;
+        const int32_t e_begin = wave * slice;
+        const int32_t e_end = min(p.topk, e_begin + slice);
+        const uint64_t below = (uint64_t(1) << lane) - 1;
+        // all index loads of the slice in flight at once, then all block-table
+        // lookups, then the ballots (slice <= kMaxTopk / NW entries)
+        constexpr int kSteps = kMaxTopk / (NW * 64);
+        int32_t gv[kSteps];
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k) {
+            const int32_t e = e_begin + k * 64 + lane;
+            gv[k] = e < e_end ? idx[e] : -1;
         }
-        tok1 = total;
+        int32_t row[kSteps];
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k) {
+            const int32_t g = gv[k];
+            row[k] = -1;
+            if (g >= visible) {
+                raise_error(p.err, MLA_DEVERR_INDEX);
+            } else if (g >= 0 && g % p.n_shards == s) {
+                const int32_t j = g / p.n_shards;
+                row[k] = j / kBlock < p.max_blocks ? bt[j / kBlock] : -1;  // block id for now
+                row[k] = row[k] >= 0 && row[k] < p.pool_blocks ? row[k] * kBlock + (j % kBlock) : -2;
+            }
+        }
+        int cnt = 0;
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k) {
+            if (row[k] == -2) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
+            const uint64_t mask = __ballot(row[k] >= 0);
+            if (row[k] >= 0) sm.rows[e_begin + cnt + __popcll(mask & below)] = row[k];
+            cnt += __popcll(mask);
+        }
+        if (lane == 0) sm.wave_cnt[wave] = cnt;
+        __syncthreads();
+        int base = 0;
+        total_owned = 0;
+        for (int w = 0; w < NW; ++w) {
+            const int c = sm.wave_cnt[w];
+            if (w < wave) base += c;
+            total_owned += c;
+        }
+        // Move every wave's entries to their final position.  A later wave's
+        // destination can overlap an earlier wave's source, so all waves
+        // read first, then all write.
+        constexpr int kPerLane = kMaxTopk / (NW * 64);  // slice <= kMaxTopk / NW
+        int32_t mine[kPerLane];
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const int i = k * 64 + lane;
+            mine[k] = i < cnt ? sm.rows[e_begin + i] : 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const int i = k * 64 + lane;
+            if (i < cnt) sm.rows[base + i] = mine[k];
+        }
+        __syncthreads();
+        tok1 = total_owned;
     }
     const int n_sub = tok1 > tok0 ? (tok1 - tok0 + kSub - 1) / kSub : 0;
     // the pipelined loop is unrolled by the ring size and always runs whole
