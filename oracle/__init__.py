@@ -26,6 +26,12 @@ What it computes, with the page each part follows:
   neutral (0, -inf) row of a shard that owns none of a row's selections:
   "GLM-5.2 vLLM Decode Context Parallelism", section "Separate the backend
   merge from stable".
+* Writing new tokens into the sharded cache: the owning shard's slot of each
+  token (a negative slot suppresses the cache write, never the query: "GLM-5.2
+  vLLM Decode Context Parallelism", section "Keep the current-main
+  correctness blocker visible") and the row it receives in the cache's
+  storage format, with the fp8 codes chosen by a per-group scale and
+  round-to-nearest-even (a reading; the pages give no quantiser).
 
 Every function states the passage it follows.  Where the pages leave a step
 open, the reading taken is stated at the function.
@@ -33,9 +39,10 @@ open, the reading taken is stated at the function.
 Pins (tests marked ``not gpu``): closed forms of softmax attention, the
 partition invariant of the merge against an independent library attention
 (torch scaled_dot_product_attention in float64) and scipy's logsumexp, the
-OCP E4M3FN code table and torch's float8/bfloat16 casts for the codecs,
+OCP E4M3FN code table, exact rounding midpoints and torch's float8/bfloat16
+casts for the codecs and encoders,
 brute-force enumeration for the integer steps, and the tables the pages
 print (copy geometry, head envelope, per-token byte counts).
 """
 
-from . import codecs, sharding, attention, capacity, decode  # noqa: F401
+from . import codecs, sharding, attention, capacity, decode, kv_write  # noqa: F401
