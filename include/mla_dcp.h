@@ -18,7 +18,7 @@
  * ---------------------------------------
  * - Tensor arguments are DEVICE pointers unless stated otherwise.  The caller
  *   owns all memory; the library keeps no pointer after a call returns and
- *   allocates no device memory inside the decode, merge and localise calls.
+ *   allocates no device memory inside any call.
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
  *   is enqueued asynchronously on it; inputs must stay valid and outputs
  *   untouched until it completes.
@@ -56,7 +56,8 @@
  * A block-table row too narrow for a request's local length, a block id
  * outside [0, pool_blocks), or a top-K index outside the query token's causal
  * prefix sets a bit in the first 32-bit word of the workspace; the offending
- * tokens are skipped (treated as not attended).  The word is sticky: it is
+ * tokens are skipped (treated as not attended).  The cache-write calls report
+ * their own bad entries the same way (the write is skipped).  The word is sticky: it is
  * cleared only by mla_clear_device_error, and read by mla_get_device_error.
  */
 #ifndef MLA_DCP_H
@@ -87,6 +88,7 @@ extern "C" {
 /* Bits of the device error word. */
 #define MLA_DEVERR_BLOCK_TABLE 1u /* table too narrow, or block id out of pool */
 #define MLA_DEVERR_INDEX 2u       /* top-K index beyond the causal prefix      */
+#define MLA_DEVERR_SLOT 4u        /* cache-write slot at or past the pool end  */
 
 /* Shape of one decode step.  Fixed by this build: kv_lora_rank = 512,
  * rope_dim = 64, block_size = 64; num_heads in {16, 32, 64, 128} (the query
@@ -181,6 +183,58 @@ int32_t mla_lse_merge(int32_t n_parts, int64_t rows, int32_t dv, int32_t part_dt
  * count >= 0 int32 entries; bit-exact. */
 int32_t mla_localize_indices(const int32_t* global_idx, int64_t count, int32_t shard_id,
                              int32_t n_shards, int32_t* local_idx, void* stream);
+
+/* Cache slots of new tokens under round-robin ownership ("How vLLM Serves
+ * GLM-5.3 with Million-Token Contexts on 16 H200s", section "The core
+ * design"): token i of request b = req_idx[i] at global position
+ * p = positions[i] belongs to shard s = p mod n_shards as its local token
+ * j = p div n_shards, stored in row j mod 64 of pool block
+ * block_tables[s - shard_begin][b][j / 64].  For tokens owned by a shard in
+ * shard_begin .. shard_begin + shard_count - 1:
+ *   slot_mapping[i] = block * 64 + j mod 64
+ * and for every other token -1: a token another rank owns, or padding
+ * (p < 0, or b outside [0, batch)).  A table row too narrow for j, or a block
+ * id outside [0, pool_blocks), gives -1 and sets MLA_DEVERR_BLOCK_TABLE in
+ * the error word.  shard_count = 1 is the call one DCP rank makes;
+ * shard_count = n_shards gives every token its owner's slot in one pool
+ * shared by all shards (the one-GPU emulation).
+ *   req_idx, positions  [n_tokens] int32
+ *   block_tables        [shard_count][batch][max_blocks] int32
+ *   slot_mapping        [n_tokens] int64 (output, 8-byte aligned)
+ *   workspace           NULL, or a buffer whose first 32-bit word is the
+ *                       sticky device error word (as for decode)
+ * Bit-exact integer work.  n_tokens >= 0; batch, max_blocks, pool_blocks >= 1. */
+int32_t mla_dcp_slot_mapping(const int32_t* req_idx, const int32_t* positions, int64_t n_tokens,
+                             const int32_t* block_tables, int32_t batch, int32_t max_blocks,
+                             int64_t pool_blocks, int32_t shard_begin, int32_t shard_count,
+                             int32_t n_shards, int64_t* slot_mapping, void* workspace,
+                             void* stream);
+
+/* Write new tokens into the paged pool at their slots.  Token i's 576 values
+ * (512 latent, then 64 rope) go to row slot_mapping[i] in kv_dtype's row
+ * format (see "Layouts"); a negative slot writes nothing.  With DCP a
+ * negative slot marks a token whose KV another rank owns: ownership
+ * suppresses only the cache write, never the token's query work, which this
+ * call does not touch ("GLM-5.2 vLLM Decode Context Parallelism", section
+ * "Keep the current-main correctness blocker visible").  A slot at or past
+ * pool_blocks * 64 writes nothing and sets MLA_DEVERR_SLOT.
+ *   kv_new        [n_tokens][576] src_dtype (MLA_F32 or MLA_BF16), 16-byte aligned
+ *   slot_mapping  [n_tokens] int64, 8-byte aligned; non-negative slots must
+ *                 be distinct (a repeated slot leaves that row unspecified)
+ *   kv_pool       [pool_blocks][64][row] kv_dtype, 16-byte aligned
+ *   workspace     NULL, or a buffer whose first 32-bit word is the error word
+ * Conversions: f32 -> bf16 rounds to nearest even; bf16 -> f32 is exact.
+ * MLA_FP8_DS rows (the pages' packed fp8 cache, "GLM-5.2 vLLM Decode Context
+ * Parallelism", section "Understand the cache-copy opportunity"; the
+ * quantiser itself is not on the pages): per 128-dim group g,
+ *   scale_g = max |x| / 448 in float32 (1 if the group is all zero),
+ *   code[d] = E4M3FN(x[d] / scale_g) rounded to nearest even, saturating at
+ *             +-448 (float32 IEEE division),
+ * and the rope part is stored as bf16.  Inputs must be finite.  Codes,
+ * scales and rows are bit-exact functions of the input.  n_tokens >= 0. */
+int32_t mla_kv_write(const void* kv_new, int32_t src_dtype, int64_t n_tokens,
+                     const int64_t* slot_mapping, int32_t kv_dtype, void* kv_pool,
+                     int64_t pool_blocks, void* workspace, void* stream);
 
 /* Read the device error word of a workspace: waits for `stream`, then copies
  * the word to *code_out (0 = no error; else MLA_DEVERR_* bits). */

@@ -13,7 +13,7 @@ import torch
 
 from . import _lib
 from ._lib import (MLA_BF16, MLA_F32, MLA_FP8_DS, MLA_DEVERR_BLOCK_TABLE,  # noqa: F401
-                   MLA_DEVERR_INDEX, MLADecodeDesc)
+                   MLA_DEVERR_INDEX, MLA_DEVERR_SLOT, MLADecodeDesc)
 
 DTYPE_CODES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8_ds": MLA_FP8_DS}
 LATENT = 512
@@ -117,6 +117,27 @@ def mla_localize_indices(global_idx, shard_id, n_shards, local_idx, stream=None)
     _check(_lib.load().mla_localize_indices(
         _ptr(global_idx), global_idx.numel(), shard_id, n_shards, _ptr(local_idx),
         _stream(stream)), "mla_localize_indices")
+
+
+def mla_dcp_slot_mapping(req_idx, positions, block_tables, shard_begin, n_shards, pool_blocks,
+                         slot_mapping, workspace=None, stream=None):
+    """req_idx, positions [T] int32; block_tables [shard_count][B][max_blocks] int32
+    -> slot_mapping [T] int64 (-1 where no shard in the range writes the token)."""
+    shard_count, batch, max_blocks = block_tables.shape
+    _check(_lib.load().mla_dcp_slot_mapping(
+        _ptr(req_idx), _ptr(positions), positions.numel(), _ptr(block_tables), batch, max_blocks,
+        pool_blocks, shard_begin, shard_count, n_shards, _ptr(slot_mapping), _ptr(workspace),
+        _stream(stream)), "mla_dcp_slot_mapping")
+
+
+def mla_kv_write(kv_new, slot_mapping, kv_pool, kv_dtype, pool_blocks, workspace=None,
+                 stream=None):
+    """kv_new [T][576] f32/bf16, slot_mapping [T] int64 -> rows of kv_pool (in place)."""
+    code = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}
+    _check(_lib.load().mla_kv_write(
+        _ptr(kv_new), code[kv_new.dtype], slot_mapping.numel(), _ptr(slot_mapping),
+        DTYPE_CODES.get(kv_dtype, kv_dtype), _ptr(kv_pool), pool_blocks, _ptr(workspace),
+        _stream(stream)), "mla_kv_write")
 
 
 def mla_get_device_error(workspace, stream=None):

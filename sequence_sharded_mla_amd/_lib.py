@@ -25,6 +25,7 @@ MLA_FP8_DS = 2
 
 MLA_DEVERR_BLOCK_TABLE = 1
 MLA_DEVERR_INDEX = 2
+MLA_DEVERR_SLOT = 4
 
 
 class MLADecodeDesc(ctypes.Structure):
@@ -62,6 +63,9 @@ SIGNATURES = {
                                          _vp, _vp, _i64, _vp]),
     "mla_lse_merge": (_i32, [_i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp]),
     "mla_localize_indices": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp]),
+    "mla_dcp_slot_mapping": (_i32, [_vp, _vp, _i64, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _vp,
+                                    _vp, _vp]),
+    "mla_kv_write": (_i32, [_vp, _i32, _i64, _vp, _i32, _vp, _i64, _vp, _vp]),
     "mla_get_device_error": (_i32, [_vp, ctypes.POINTER(_i32), _vp]),
     "mla_clear_device_error": (_i32, [_vp, _vp]),
 }

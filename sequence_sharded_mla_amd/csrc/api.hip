@@ -6,6 +6,7 @@
 #include "decode_fp8.hpp"
 #include "decode_mfma.hpp"
 #include "decode_valu.hpp"
+#include "kv_write.hpp"
 #include "params.hpp"
 #include "plan.hpp"
 #include "reduce.hpp"
@@ -185,6 +186,81 @@ int32_t mla_localize_indices(const int32_t* global_idx, int64_t count, int32_t s
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(mla::localize_kernel, dim3(uint32_t(blocks)), dim3(256), 0,
                        mla::as_stream(stream), global_idx, count, shard_id, n_shards, local_idx);
+    return mla::launch_status();
+}
+
+int32_t mla_dcp_slot_mapping(const int32_t* req_idx, const int32_t* positions, int64_t n_tokens,
+                             const int32_t* block_tables, int32_t batch, int32_t max_blocks,
+                             int64_t pool_blocks, int32_t shard_begin, int32_t shard_count,
+                             int32_t n_shards, int64_t* slot_mapping, void* workspace,
+                             void* stream) {
+    if (n_tokens < 0 || n_tokens > INT32_MAX || batch < 1 || max_blocks < 1 || pool_blocks < 1 ||
+        pool_blocks > (int64_t(1) << 40))
+        return MLA_ERR_SHAPE;
+    if (n_shards < 1 || shard_begin < 0 || shard_count < 1 || shard_begin + shard_count > n_shards)
+        return MLA_ERR_SHARD;
+    if (n_tokens == 0) return MLA_OK;
+    if (!req_idx || !positions || !block_tables || !slot_mapping) return MLA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) || (reinterpret_cast<uintptr_t>(req_idx) & 3u) ||
+        (reinterpret_cast<uintptr_t>(positions) & 3u) || (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 3u))
+        return MLA_ERR_ALIGN;
+    mla::kvw::SlotParams p{};
+    p.req_idx = req_idx;
+    p.positions = positions;
+    p.block_tables = block_tables;
+    p.slots = slot_mapping;
+    p.err = static_cast<uint32_t*>(workspace);
+    p.n = n_tokens;
+    p.pool_blocks = pool_blocks;
+    p.B = batch;
+    p.max_blocks = max_blocks;
+    p.shard_begin = shard_begin;
+    p.shard_count = shard_count;
+    p.n_shards = n_shards;
+    int64_t blocks = (n_tokens + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(mla::kvw::slot_mapping_kernel, dim3(uint32_t(blocks)), dim3(256), 0,
+                       mla::as_stream(stream), p);
+    return mla::launch_status();
+}
+
+int32_t mla_kv_write(const void* kv_new, int32_t src_dtype, int64_t n_tokens,
+                     const int64_t* slot_mapping, int32_t kv_dtype, void* kv_pool,
+                     int64_t pool_blocks, void* workspace, void* stream) {
+    if (n_tokens < 0 || n_tokens > INT32_MAX || pool_blocks < 1 || pool_blocks > (int64_t(1) << 40))
+        return MLA_ERR_SHAPE;
+    if ((src_dtype != MLA_F32 && src_dtype != MLA_BF16) ||
+        (kv_dtype != MLA_F32 && kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_DS))
+        return MLA_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return MLA_OK;
+    if (!kv_new || !slot_mapping || !kv_pool) return MLA_ERR_NULL;
+    if (!mla::aligned16(kv_new) || !mla::aligned16(kv_pool) ||
+        (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+        return MLA_ERR_ALIGN;
+    mla::kvw::WriteParams p{};
+    p.src = static_cast<const uint8_t*>(kv_new);
+    p.slots = slot_mapping;
+    p.pool = static_cast<uint8_t*>(kv_pool);
+    p.err = static_cast<uint32_t*>(workspace);
+    p.n = n_tokens;
+    p.pool_rows = pool_blocks * mla::kBlock;
+    int64_t blocks = (n_tokens + mla::kvw::kWaves - 1) / mla::kvw::kWaves;
+    if (blocks > 65536) blocks = 65536;
+    const dim3 grid(static_cast<uint32_t>(blocks));
+    hipStream_t s = mla::as_stream(stream);
+    using namespace mla::kvw;
+#define MLA_KVW_LAUNCH(S, K) hipLaunchKernelGGL((kv_write_kernel<S, K>), grid, dim3(256), 0, s, p)
+    if (src_dtype == MLA_BF16) {
+        if (kv_dtype == MLA_FP8_DS) MLA_KVW_LAUNCH(MLA_BF16, MLA_FP8_DS);
+        else if (kv_dtype == MLA_BF16) MLA_KVW_LAUNCH(MLA_BF16, MLA_BF16);
+        else MLA_KVW_LAUNCH(MLA_BF16, MLA_F32);
+    } else {
+        if (kv_dtype == MLA_FP8_DS) MLA_KVW_LAUNCH(MLA_F32, MLA_FP8_DS);
+        else if (kv_dtype == MLA_BF16) MLA_KVW_LAUNCH(MLA_F32, MLA_BF16);
+        else MLA_KVW_LAUNCH(MLA_F32, MLA_F32);
+    }
+#undef MLA_KVW_LAUNCH
     return mla::launch_status();
 }
 

@@ -199,3 +199,53 @@ def test_merge_and_localize_checks(lib):
     code = ctypes.c_int32()
     assert lib.mla_get_device_error(None, ctypes.byref(code), None) == _lib.MLA_ERR_NULL
     assert lib.mla_clear_device_error(None, None) == _lib.MLA_ERR_NULL
+
+
+def test_slot_mapping_checks(lib):
+    v = ctypes.c_void_p
+
+    def sm(n=10, B=2, mb=4, pool=100, begin=0, count=8, N=8, req=FAKE, pos=FAKE, bt=FAKE,
+           out=FAKE, ws=None):
+        return lib.mla_dcp_slot_mapping(v(req), v(pos), n, v(bt), B, mb, pool, begin, count, N,
+                                        v(out), None if ws is None else v(ws), None)
+
+    assert sm(n=-1) == _lib.MLA_ERR_SHAPE
+    assert sm(n=1 << 31) == _lib.MLA_ERR_SHAPE
+    assert sm(B=0) == _lib.MLA_ERR_SHAPE
+    assert sm(mb=0) == _lib.MLA_ERR_SHAPE
+    assert sm(pool=0) == _lib.MLA_ERR_SHAPE
+    assert sm(N=0, count=1) == _lib.MLA_ERR_SHARD
+    assert sm(begin=1) == _lib.MLA_ERR_SHARD
+    assert sm(begin=-1, count=1) == _lib.MLA_ERR_SHARD
+    assert sm(count=0) == _lib.MLA_ERR_SHARD
+    assert sm(req=None) == _lib.MLA_ERR_NULL
+    assert sm(pos=None) == _lib.MLA_ERR_NULL
+    assert sm(bt=None) == _lib.MLA_ERR_NULL
+    assert sm(out=None) == _lib.MLA_ERR_NULL
+    assert sm(out=FAKE + 4) == _lib.MLA_ERR_ALIGN
+    assert sm(pos=FAKE + 2) == _lib.MLA_ERR_ALIGN
+    assert sm(ws=FAKE + 2) == _lib.MLA_ERR_ALIGN
+    assert sm(n=0, req=None, pos=None, bt=None, out=None) == 0
+
+
+def test_kv_write_checks(lib):
+    v = ctypes.c_void_p
+
+    def kw(src=FAKE, sd=_lib.MLA_BF16, n=10, slots=FAKE, kd=_lib.MLA_FP8_DS, pool=FAKE,
+           blocks=100, ws=None):
+        return lib.mla_kv_write(v(src), sd, n, v(slots), kd, v(pool), blocks,
+                                None if ws is None else v(ws), None)
+
+    assert kw(n=-1) == _lib.MLA_ERR_SHAPE
+    assert kw(n=1 << 31) == _lib.MLA_ERR_SHAPE
+    assert kw(blocks=0) == _lib.MLA_ERR_SHAPE
+    assert kw(sd=_lib.MLA_FP8_DS) == _lib.MLA_ERR_UNSUPPORTED
+    assert kw(kd=3) == _lib.MLA_ERR_UNSUPPORTED
+    assert kw(src=None) == _lib.MLA_ERR_NULL
+    assert kw(slots=None) == _lib.MLA_ERR_NULL
+    assert kw(pool=None) == _lib.MLA_ERR_NULL
+    assert kw(src=FAKE + 8) == _lib.MLA_ERR_ALIGN
+    assert kw(pool=FAKE + 8) == _lib.MLA_ERR_ALIGN
+    assert kw(slots=FAKE + 4) == _lib.MLA_ERR_ALIGN
+    assert kw(ws=FAKE + 1) == _lib.MLA_ERR_ALIGN
+    assert kw(n=0, src=None, slots=None, pool=None) == 0

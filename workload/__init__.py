@@ -236,3 +236,30 @@ def generate(spec, threads=None):
                   row_pos=row_pos, latent=latent, scales=scales, rope=rope,
                   topk_idx=topk_idx, layout_seed=spec.seed * 7919 + 17,
                   dense=not spec.topk)
+
+
+# Cache writes: new tokens' rows (latent + rope) as a model layer hands them
+# to the cache.  The long-context write stands in for filling one request's
+# 1M-token cache (the shape of long_fp8_1m) from bf16 activations, with the
+# tokens dealt round-robin over 8 shards.
+WRITE_SPECS = {
+    "kv_write_fp8_1m": dict(tokens=1048576, n_shards=8, src_dtype="bf16", kv_dtype="fp8_ds",
+                            seed=606),
+}
+
+
+def new_token_rows(n, seed, dtype="bf16", spread=0):
+    """Seeded [n, 576] rows of new cache tokens: float32, or uint16 bf16 bits.
+
+    Entries are N(0, 1); with spread > 0 each row is multiplied by 2^k, k a
+    uniform integer in [-spread, spread], so group maxima span many binades.
+    """
+    out = np.empty((n, DK), np.float32 if dtype == "f32" else np.uint16)
+    for r0 in range(0, n, SLICE):
+        m = min(SLICE, n - r0)
+        rng = np.random.default_rng([seed, 7, r0 // SLICE])
+        x = rng.standard_normal((m, DK), dtype=np.float32)
+        if spread:
+            x *= np.exp2(rng.integers(-spread, spread + 1, (m, 1))).astype(np.float32)
+        out[r0:r0 + m] = x if dtype == "f32" else _bf16_bits(x)
+    return out
