@@ -31,18 +31,27 @@ METRIC = "MLA decode attention: achieved HBM GB/s (% of peak) and KV tokens/s at
 KERNEL_SOURCES = ["decode_valu.hpp", "decode_mfma.hpp", "decode_fp8.hpp", "mfma_common.hpp", "common.hpp",
                   "params.hpp", "api.hip",
                   "reduce.hpp", "plan.hpp", "host.cpp"]
+WRITE_SOURCES = ["kv_write.hpp", "common.hpp", "api.hip"]
+WRITE_METRIC = "DCP KV cache write: achieved HBM GB/s (% of peak) and tokens/s, 1M tokens over 8 shards"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash():
+def kernel_hash(sources=KERNEL_SOURCES):
+    """Hash of the kernel sources with comments and blank lines removed, so
+    that recorded counters stay valid across comment-only edits."""
+    import re
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         p = os.path.join(ROOT, "sequence_sharded_mla_amd", "csrc", name)
         if os.path.exists(p):
-            h.update(open(p, "rb").read())
+            text = open(p).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+            lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+            h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 
@@ -104,6 +113,142 @@ def traffic_for(workload, khash):
     return rec.get("bytes_per_launch")
 
 
+def write_bytes_per_token(src_dtype, kv_dtype):
+    """Algorithmic bytes of one written token: source row, request id and
+    position (int32 each), cache row."""
+    from sequence_sharded_mla_amd.layout import ROW_BYTES
+    return (576 * (2 if src_dtype == "bf16" else 4)) + 4 + 4 + ROW_BYTES[kv_dtype]
+
+
+def write_cpu_baseline(src, tables, w, budget_s=10.0):
+    """Time the oracle's slot mapping + row encoding on a prefix of the tokens."""
+    from oracle import kv_write as okw
+    n_shards = w["n_shards"]
+    pool_blocks = int(tables.max()) + 1
+    done, chunk, t0 = 0, 256, time.perf_counter()
+    while done < src.shape[0] and (time.perf_counter() - t0) < budget_s:
+        rows = src[done:done + chunk]
+        f = (rows.astype(np.uint32) << 16).view(np.float32) if w["src_dtype"] == "bf16" else rows
+        pos = np.arange(done, done + rows.shape[0])
+        slots, _ = okw.dcp_slot_mapping(np.zeros(pos.size, np.int64), pos, tables, 0, n_shards,
+                                        n_shards, pool_blocks)
+        for i in range(rows.shape[0]):
+            okw.row_bytes_for(f[i], w["kv_dtype"])
+        done += rows.shape[0]
+    dt = time.perf_counter() - t0
+    per = write_bytes_per_token(w["src_dtype"], w["kv_dtype"])
+    return {"value": round(done * per / dt / 1e9, 6), "unit": "GB/s",
+            "tokens_per_s": round(done / dt, 1), "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {src.shape[0]} tokens (slot mapping + row encoding), {dt:.1f} s"}
+
+
+def time_launches(fn, K, stream):
+    import torch
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(K)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def run_kv_write(args):
+    """Cache write of one request's 1M new tokens, dealt over 8 shards held in
+    one pool: the fused owner-slot + quantise-and-store call (one launch)."""
+    import torch
+    import workload
+    from sequence_sharded_mla_amd import (layout, mla_clear_device_error, mla_dcp_kv_write,
+                                          mla_dcp_slot_mapping, mla_get_device_error, mla_kv_write)
+    name = "kv_write_fp8_1m"
+    w = workload.WRITE_SPECS[name]
+    T, N, kv = w["tokens"], w["n_shards"], w["kv_dtype"]
+    log(f"bench: generating {name}")
+    src = workload.new_token_rows(T, seed=w["seed"], dtype=w["src_dtype"])
+    tables, blocks = layout.build_block_tables(np.array([T]), N, seed=w["seed"])
+    rb = layout.ROW_BYTES[kv]
+    d_src = torch.from_numpy(src.view(np.int16)).cuda().view(torch.bfloat16)
+    d_req = torch.zeros(T, dtype=torch.int32, device="cuda")
+    d_pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    d_tab = torch.from_numpy(tables).cuda()
+    d_tab0 = torch.from_numpy(np.ascontiguousarray(tables[:1])).cuda()
+    d_slots = torch.empty(T, dtype=torch.int64, device="cuda")
+    pool = torch.zeros(blocks * 64 * rb, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    mla_clear_device_error(ws)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mla_dcp_kv_write(d_src, d_req, d_pos, d_tab, 0, N, pool, kv, blocks, workspace=ws)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    log(f"bench: timing {K} steps")
+    t0 = time.perf_counter()
+    t_step = time_launches(step, K, stream)
+    wall = time.perf_counter() - t0
+    # the same write as two calls (slot array, then write) and one rank's call
+    extras = not args.no_extras
+    nan = np.array([np.nan])
+    t_map = time_launches(lambda: mla_dcp_slot_mapping(d_req, d_pos, d_tab, 0, N, blocks, d_slots,
+                                                       workspace=ws), K, stream) if extras else nan
+    t_two = time_launches(lambda: mla_kv_write(d_src, d_slots, pool, kv, blocks, workspace=ws), K,
+                          stream) if extras else nan
+    t_rank = time_launches(lambda: mla_dcp_kv_write(d_src, d_req, d_pos, d_tab0, 0, N, pool, kv, blocks,
+                                                    workspace=ws), K, stream) if extras else nan
+    assert mla_get_device_error(ws) == 0
+    ms_step = wall * 1e3 / K
+    per = write_bytes_per_token(w["src_dtype"], kv)
+    launch_bytes = T * per + tables.size * 4
+    wr_ms = float(np.mean(t_step))
+    achieved = launch_bytes / (wr_ms * 1e-3) / 1e9
+    gbs = launch_bytes / (ms_step * 1e-3) / 1e9
+    khash = kernel_hash(WRITE_SOURCES)
+    rank_bytes = (T // N) * (per - 8) + T * 8 + tables[:1].size * 4
+    rec = {
+        "metric": WRITE_METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) bf16 rows, random-permuted paged blocks)",
+        "config": {"workload": name, "tokens": T, "n_shards": N, "source": w["src_dtype"],
+                   "kv_cache": kv, "block_size": 64},
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": int(launch_bytes),
+        "kernels_ms": {"dcp_kv_write": round(wr_ms, 4),
+                       "dcp_kv_write_p10_p90": [round(float(np.percentile(t_step, 10)), 4),
+                                                round(float(np.percentile(t_step, 90)), 4)],
+                       "two_calls": {"slot_mapping": round(float(np.mean(t_map)), 4),
+                                     "kv_write": round(float(np.mean(t_two)), 4)} if extras else None,
+                       "one_rank_of_8": round(float(np.mean(t_rank)), 4) if extras else None,
+                       "one_rank_of_8_gbs": round(rank_bytes / (float(np.mean(t_rank)) * 1e-3) / 1e9, 1)
+                       if extras else None},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for(name, khash),
+                     "kernel": "kv_write_kernel<bf16, fp8_ds, fused> (all shards, one launch)",
+                     "algorithmic_bytes_per_launch": int(launch_bytes)},
+        "kernel_hash": khash,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host")
+        rec["cpu_baseline"] = write_cpu_baseline(src, tables, w, args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +257,11 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--kv-write", action="store_true",
+                    help="time the cache write (owner slot mapping + quantise-and-store) instead "
+                         "of the decode step")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="with --kv-write: time only the fused all-shard call (for profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     args = ap.parse_args()
@@ -129,6 +279,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.kv_write:
+        run_kv_write(args)
         return
     import workload
     from sequence_sharded_mla_amd import layout, mla_get_device_error

@@ -236,6 +236,20 @@ int32_t mla_kv_write(const void* kv_new, int32_t src_dtype, int64_t n_tokens,
                      const int64_t* slot_mapping, int32_t kv_dtype, void* kv_pool,
                      int64_t pool_blocks, void* workspace, void* stream);
 
+/* mla_dcp_slot_mapping and mla_kv_write in one launch: each token's slot is
+ * computed from req_idx, positions and the shards' block tables exactly as
+ * mla_dcp_slot_mapping defines it, and the token's row is written there as
+ * mla_kv_write defines it; tokens no shard in the range owns (or padding)
+ * are skipped without reading their source row.  Table errors set
+ * MLA_DEVERR_BLOCK_TABLE.  Arguments as in those two calls; no slot array
+ * is read or written.  Knowing the share of tokens its shards own, the call
+ * sizes its grid so each wave gathers about eight written tokens. */
+int32_t mla_dcp_kv_write(const void* kv_new, int32_t src_dtype, const int32_t* req_idx,
+                         const int32_t* positions, int64_t n_tokens, const int32_t* block_tables,
+                         int32_t batch, int32_t max_blocks, int32_t shard_begin, int32_t shard_count,
+                         int32_t n_shards, int32_t kv_dtype, void* kv_pool, int64_t pool_blocks,
+                         void* workspace, void* stream);
+
 /* Read the device error word of a workspace: waits for `stream`, then copies
  * the word to *code_out (0 = no error; else MLA_DEVERR_* bits). */
 int32_t mla_get_device_error(const void* workspace, int32_t* code_out, void* stream);

@@ -140,6 +140,18 @@ def mla_kv_write(kv_new, slot_mapping, kv_pool, kv_dtype, pool_blocks, workspace
         _stream(stream)), "mla_kv_write")
 
 
+def mla_dcp_kv_write(kv_new, req_idx, positions, block_tables, shard_begin, n_shards, kv_pool,
+                     kv_dtype, pool_blocks, workspace=None, stream=None):
+    """Owner slot mapping and row write in one launch (see mla_dcp_slot_mapping, mla_kv_write)."""
+    code = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}
+    shard_count, batch, max_blocks = block_tables.shape
+    _check(_lib.load().mla_dcp_kv_write(
+        _ptr(kv_new), code[kv_new.dtype], _ptr(req_idx), _ptr(positions), positions.numel(),
+        _ptr(block_tables), batch, max_blocks, shard_begin, shard_count, n_shards,
+        DTYPE_CODES.get(kv_dtype, kv_dtype), _ptr(kv_pool), pool_blocks, _ptr(workspace),
+        _stream(stream)), "mla_dcp_kv_write")
+
+
 def mla_get_device_error(workspace, stream=None):
     code = ctypes.c_int32(0)
     _check(_lib.load().mla_get_device_error(_ptr(workspace), ctypes.byref(code), _stream(stream)),

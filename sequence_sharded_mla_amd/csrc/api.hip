@@ -119,6 +119,85 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     return MLA_OK;
 }
 
+
+int32_t make_slot_params(const int32_t* req_idx, const int32_t* positions, int64_t n_tokens,
+                         const int32_t* block_tables, int32_t batch, int32_t max_blocks,
+                         int64_t pool_blocks, int32_t shard_begin, int32_t shard_count, int32_t n_shards,
+                         void* workspace, kvw::SlotParams* p) {
+    if (n_tokens < 0 || n_tokens > INT32_MAX || batch < 1 || max_blocks < 1 || pool_blocks < 1 ||
+        pool_blocks > (int64_t(1) << 40))
+        return MLA_ERR_SHAPE;
+    if (n_shards < 1 || shard_begin < 0 || shard_count < 1 || shard_begin + shard_count > n_shards)
+        return MLA_ERR_SHARD;
+    if (n_tokens == 0) return MLA_OK;
+    if (!req_idx || !positions || !block_tables) return MLA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(req_idx) & 3u) || (reinterpret_cast<uintptr_t>(positions) & 3u) ||
+        (reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+        return MLA_ERR_ALIGN;
+    p->req_idx = req_idx;
+    p->positions = positions;
+    p->block_tables = block_tables;
+    p->err = static_cast<uint32_t*>(workspace);
+    p->n = n_tokens;
+    p->pool_blocks = pool_blocks;
+    p->B = batch;
+    p->max_blocks = max_blocks;
+    p->shard_begin = shard_begin;
+    p->shard_count = shard_count;
+    p->n_shards = n_shards;
+    return MLA_OK;
+}
+
+int32_t check_write(const void* kv_new, int32_t src_dtype, int64_t n_tokens, int32_t kv_dtype,
+                    const void* kv_pool, int64_t pool_blocks, const void* workspace) {
+    if (n_tokens < 0 || n_tokens > INT32_MAX || pool_blocks < 1 || pool_blocks > (int64_t(1) << 40))
+        return MLA_ERR_SHAPE;
+    if ((src_dtype != MLA_F32 && src_dtype != MLA_BF16) ||
+        (kv_dtype != MLA_F32 && kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_DS))
+        return MLA_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return MLA_OK;
+    if (!kv_new || !kv_pool) return MLA_ERR_NULL;
+    if (!aligned16(kv_new) || !aligned16(kv_pool) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+        return MLA_ERR_ALIGN;
+    return MLA_OK;
+}
+
+// chunks_per_wave: how many 8-token chunks one wave scans (1..8).
+int32_t launch_write(kvw::WriteParams p, const void* kv_new, int32_t src_dtype, int64_t n_tokens,
+                     int32_t kv_dtype, void* kv_pool, int64_t pool_blocks, void* workspace,
+                     int32_t chunks_per_wave, bool fused, void* stream) {
+    p.src = static_cast<const uint8_t*>(kv_new);
+    p.pool = static_cast<uint8_t*>(kv_pool);
+    p.err = static_cast<uint32_t*>(workspace);
+    p.n = n_tokens;
+    p.pool_rows = pool_blocks * kBlock;
+    const int64_t chunks = (n_tokens + 7) / 8;
+    const int64_t waves = (chunks + chunks_per_wave - 1) / chunks_per_wave;
+    int64_t blocks = (waves + kvw::kWaves - 1) / kvw::kWaves;
+    if (blocks > (int64_t(1) << 22)) blocks = int64_t(1) << 22;
+    const dim3 grid(static_cast<uint32_t>(blocks));
+    hipStream_t s = as_stream(stream);
+    using kvw::kv_write_kernel;
+#define MLA_KVW_LAUNCH(S, K)                                                                  \
+    do {                                                                                      \
+        if (fused)                                                                            \
+            hipLaunchKernelGGL((kv_write_kernel<S, K, true>), grid, dim3(256), 0, s, p);      \
+        else                                                                                  \
+            hipLaunchKernelGGL((kv_write_kernel<S, K, false>), grid, dim3(256), 0, s, p);     \
+    } while (0)
+    if (src_dtype == MLA_BF16) {
+        if (kv_dtype == MLA_FP8_DS) MLA_KVW_LAUNCH(MLA_BF16, MLA_FP8_DS);
+        else if (kv_dtype == MLA_BF16) MLA_KVW_LAUNCH(MLA_BF16, MLA_BF16);
+        else MLA_KVW_LAUNCH(MLA_BF16, MLA_F32);
+    } else {
+        if (kv_dtype == MLA_FP8_DS) MLA_KVW_LAUNCH(MLA_F32, MLA_FP8_DS);
+        else if (kv_dtype == MLA_BF16) MLA_KVW_LAUNCH(MLA_F32, MLA_BF16);
+        else MLA_KVW_LAUNCH(MLA_F32, MLA_F32);
+    }
+#undef MLA_KVW_LAUNCH
+    return launch_status();
+}
+
 }  // namespace
 }  // namespace mla
 
@@ -194,30 +273,13 @@ int32_t mla_dcp_slot_mapping(const int32_t* req_idx, const int32_t* positions, i
                              int64_t pool_blocks, int32_t shard_begin, int32_t shard_count,
                              int32_t n_shards, int64_t* slot_mapping, void* workspace,
                              void* stream) {
-    if (n_tokens < 0 || n_tokens > INT32_MAX || batch < 1 || max_blocks < 1 || pool_blocks < 1 ||
-        pool_blocks > (int64_t(1) << 40))
-        return MLA_ERR_SHAPE;
-    if (n_shards < 1 || shard_begin < 0 || shard_count < 1 || shard_begin + shard_count > n_shards)
-        return MLA_ERR_SHARD;
-    if (n_tokens == 0) return MLA_OK;
-    if (!req_idx || !positions || !block_tables || !slot_mapping) return MLA_ERR_NULL;
-    if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) || (reinterpret_cast<uintptr_t>(req_idx) & 3u) ||
-        (reinterpret_cast<uintptr_t>(positions) & 3u) || (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
-        (reinterpret_cast<uintptr_t>(workspace) & 3u))
-        return MLA_ERR_ALIGN;
     mla::kvw::SlotParams p{};
-    p.req_idx = req_idx;
-    p.positions = positions;
-    p.block_tables = block_tables;
+    int32_t st = mla::make_slot_params(req_idx, positions, n_tokens, block_tables, batch, max_blocks,
+                                       pool_blocks, shard_begin, shard_count, n_shards, workspace, &p);
+    if (st != MLA_OK || n_tokens == 0) return st;
+    if (!slot_mapping) return MLA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) return MLA_ERR_ALIGN;
     p.slots = slot_mapping;
-    p.err = static_cast<uint32_t*>(workspace);
-    p.n = n_tokens;
-    p.pool_blocks = pool_blocks;
-    p.B = batch;
-    p.max_blocks = max_blocks;
-    p.shard_begin = shard_begin;
-    p.shard_count = shard_count;
-    p.n_shards = n_shards;
     int64_t blocks = (n_tokens + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(mla::kvw::slot_mapping_kernel, dim3(uint32_t(blocks)), dim3(256), 0,
@@ -228,40 +290,33 @@ int32_t mla_dcp_slot_mapping(const int32_t* req_idx, const int32_t* positions, i
 int32_t mla_kv_write(const void* kv_new, int32_t src_dtype, int64_t n_tokens,
                      const int64_t* slot_mapping, int32_t kv_dtype, void* kv_pool,
                      int64_t pool_blocks, void* workspace, void* stream) {
-    if (n_tokens < 0 || n_tokens > INT32_MAX || pool_blocks < 1 || pool_blocks > (int64_t(1) << 40))
-        return MLA_ERR_SHAPE;
-    if ((src_dtype != MLA_F32 && src_dtype != MLA_BF16) ||
-        (kv_dtype != MLA_F32 && kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_DS))
-        return MLA_ERR_UNSUPPORTED;
-    if (n_tokens == 0) return MLA_OK;
-    if (!kv_new || !slot_mapping || !kv_pool) return MLA_ERR_NULL;
-    if (!mla::aligned16(kv_new) || !mla::aligned16(kv_pool) ||
-        (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
-        return MLA_ERR_ALIGN;
+    int32_t st = mla::check_write(kv_new, src_dtype, n_tokens, kv_dtype, kv_pool, pool_blocks, workspace);
+    if (st != MLA_OK || n_tokens == 0) return st;
+    if (!slot_mapping) return MLA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) return MLA_ERR_ALIGN;
     mla::kvw::WriteParams p{};
-    p.src = static_cast<const uint8_t*>(kv_new);
     p.slots = slot_mapping;
-    p.pool = static_cast<uint8_t*>(kv_pool);
-    p.err = static_cast<uint32_t*>(workspace);
-    p.n = n_tokens;
-    p.pool_rows = pool_blocks * mla::kBlock;
-    int64_t blocks = (n_tokens + mla::kvw::kWaves - 1) / mla::kvw::kWaves;
-    if (blocks > 65536) blocks = 65536;
-    const dim3 grid(static_cast<uint32_t>(blocks));
-    hipStream_t s = mla::as_stream(stream);
-    using namespace mla::kvw;
-#define MLA_KVW_LAUNCH(S, K) hipLaunchKernelGGL((kv_write_kernel<S, K>), grid, dim3(256), 0, s, p)
-    if (src_dtype == MLA_BF16) {
-        if (kv_dtype == MLA_FP8_DS) MLA_KVW_LAUNCH(MLA_BF16, MLA_FP8_DS);
-        else if (kv_dtype == MLA_BF16) MLA_KVW_LAUNCH(MLA_BF16, MLA_BF16);
-        else MLA_KVW_LAUNCH(MLA_BF16, MLA_F32);
-    } else {
-        if (kv_dtype == MLA_FP8_DS) MLA_KVW_LAUNCH(MLA_F32, MLA_FP8_DS);
-        else if (kv_dtype == MLA_BF16) MLA_KVW_LAUNCH(MLA_F32, MLA_BF16);
-        else MLA_KVW_LAUNCH(MLA_F32, MLA_F32);
-    }
-#undef MLA_KVW_LAUNCH
-    return mla::launch_status();
+    // any slot may be written: one chunk of 8 tokens per wave
+    return mla::launch_write(p, kv_new, src_dtype, n_tokens, kv_dtype, kv_pool, pool_blocks, workspace,
+                             1, false, stream);
+}
+
+int32_t mla_dcp_kv_write(const void* kv_new, int32_t src_dtype, const int32_t* req_idx,
+                         const int32_t* positions, int64_t n_tokens, const int32_t* block_tables,
+                         int32_t batch, int32_t max_blocks, int32_t shard_begin, int32_t shard_count,
+                         int32_t n_shards, int32_t kv_dtype, void* kv_pool, int64_t pool_blocks,
+                         void* workspace, void* stream) {
+    int32_t st = mla::check_write(kv_new, src_dtype, n_tokens, kv_dtype, kv_pool, pool_blocks, workspace);
+    if (st != MLA_OK) return st;
+    mla::kvw::WriteParams p{};
+    st = mla::make_slot_params(req_idx, positions, n_tokens, block_tables, batch, max_blocks, pool_blocks,
+                               shard_begin, shard_count, n_shards, workspace, &p.map);
+    if (st != MLA_OK || n_tokens == 0) return st;
+    // about one group of written tokens per wave: shards own 1/N of
+    // consecutive positions each
+    const int32_t per_wave = (n_shards + shard_count - 1) / shard_count;
+    return mla::launch_write(p, kv_new, src_dtype, n_tokens, kv_dtype, kv_pool, pool_blocks, workspace,
+                             per_wave > 8 ? 8 : per_wave, true, stream);
 }
 
 int32_t mla_get_device_error(const void* workspace, int32_t* code_out, void* stream) {

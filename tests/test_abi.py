@@ -249,3 +249,31 @@ def test_kv_write_checks(lib):
     assert kw(slots=FAKE + 4) == _lib.MLA_ERR_ALIGN
     assert kw(ws=FAKE + 1) == _lib.MLA_ERR_ALIGN
     assert kw(n=0, src=None, slots=None, pool=None) == 0
+
+
+def test_fused_write_checks(lib):
+    v = ctypes.c_void_p
+
+    def fw(src=FAKE, sd=_lib.MLA_BF16, req=FAKE, pos=FAKE, n=10, bt=FAKE, B=2, mb=4, begin=0,
+           count=8, N=8, kd=_lib.MLA_FP8_DS, pool=FAKE, blocks=100, ws=None):
+        return lib.mla_dcp_kv_write(v(src), sd, v(req), v(pos), n, v(bt), B, mb, begin, count, N, kd,
+                                    v(pool), blocks, None if ws is None else v(ws), None)
+
+    assert fw(n=-1) == _lib.MLA_ERR_SHAPE
+    assert fw(blocks=0) == _lib.MLA_ERR_SHAPE
+    assert fw(B=0) == _lib.MLA_ERR_SHAPE
+    assert fw(mb=0) == _lib.MLA_ERR_SHAPE
+    assert fw(sd=_lib.MLA_FP8_DS) == _lib.MLA_ERR_UNSUPPORTED
+    assert fw(kd=5) == _lib.MLA_ERR_UNSUPPORTED
+    assert fw(N=0, count=1) == _lib.MLA_ERR_SHARD
+    assert fw(begin=2) == _lib.MLA_ERR_SHARD
+    assert fw(count=0) == _lib.MLA_ERR_SHARD
+    assert fw(src=None) == _lib.MLA_ERR_NULL
+    assert fw(pool=None) == _lib.MLA_ERR_NULL
+    assert fw(req=None) == _lib.MLA_ERR_NULL
+    assert fw(pos=None) == _lib.MLA_ERR_NULL
+    assert fw(bt=None) == _lib.MLA_ERR_NULL
+    assert fw(src=FAKE + 8) == _lib.MLA_ERR_ALIGN
+    assert fw(pos=FAKE + 2) == _lib.MLA_ERR_ALIGN
+    assert fw(ws=FAKE + 2) == _lib.MLA_ERR_ALIGN
+    assert fw(n=0, src=None, req=None, pos=None, bt=None, pool=None) == 0

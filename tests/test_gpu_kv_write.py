@@ -16,7 +16,7 @@ import torch
 import workload
 from oracle import codecs, kv_write as okw
 from sequence_sharded_mla_amd import (MLA_DEVERR_BLOCK_TABLE, MLA_DEVERR_SLOT, layout,
-                                      mla_clear_device_error, mla_dcp_slot_mapping,
+                                      mla_clear_device_error, mla_dcp_kv_write, mla_dcp_slot_mapping,
                                       mla_get_device_error, mla_kv_write)
 from sequence_sharded_mla_amd.step import ShardedDecodeStep
 
@@ -80,10 +80,14 @@ def test_write_matches_oracle_bit_exact(src_dtype, kv_dtype):
         rows[3, :128] = 0.0
         rows[3, 7] = -0.0
         rows[4, 128:256] = -0.0
+        rows[5] *= np.float32(2.0 ** 110)           # group scales above 2^100
+        rows[6] *= np.float32(2.0 ** -90)           # group scales below 2^-80
     else:
         rows[3, :128] = 0
         rows[3, 7] = 0x8000
         rows[4, 128:256] = 0x8000
+        for r, k in ((5, 110), (6, -90)):           # exact power-of-two rescaling
+            rows[r] = ((host_f32(rows[r], "bf16") * np.float32(2.0 ** k)).view(np.uint32) >> 16).astype(np.uint16)
     rng = np.random.default_rng(12)
     slots = rng.permutation(blocks * 64)[:T].astype(np.int64)
     slots[::5] = -1
@@ -186,6 +190,43 @@ def test_slot_mapping_matches_oracle():
         assert mla_get_device_error(ws) == (MLA_DEVERR_BLOCK_TABLE if bad.any() else 0)
 
 
+@pytest.mark.parametrize("src_dtype,kv_dtype", [("bf16", "fp8_ds"), ("f32", "bf16"), ("bf16", "f32")])
+def test_fused_write_matches_oracle(src_dtype, kv_dtype):
+    """mla_dcp_kv_write: the oracle's slot mapping followed by its write, for
+    every shard range a rank or the emulation uses, with padding, tokens past
+    the table and a block id outside the pool."""
+    N, B, mb, pool = 8, 3, 5, 150
+    ids = np.random.default_rng(25).permutation(pool)[: N * B * mb].astype(np.int32)
+    bt = ids.reshape(N, B, mb)
+    bt[4, 2, 1] = pool + 7                          # outside the pool
+    rng = np.random.default_rng(26)
+    T = 1003                                        # not a multiple of 8 or 64
+    # distinct (request, position) pairs, so no two tokens share a slot;
+    # then padding: negative positions and request ids outside the batch
+    span = N * mb * 64 + 200
+    pick = rng.choice(B * span, T, replace=False)
+    req = (pick // span).astype(np.int32)
+    pos = (pick % span).astype(np.int32)
+    pos[rng.random(T) < 0.05] = -1
+    req[rng.random(T) < 0.03] = B
+    rows = workload.new_token_rows(T, seed=27, dtype=src_dtype, spread=6)
+    rb = ROWB[kv_dtype]
+    pool_np = np.random.default_rng(28).integers(0, 256, pool * 64 * rb, dtype=np.uint8)
+    for begin, count in [(0, 8), (0, 1), (5, 1), (2, 3)]:
+        say(f"fused write src={src_dtype} kv={kv_dtype} shards {begin}..{begin + count - 1}")
+        tab = bt[begin:begin + count]
+        ws = new_ws()
+        d_pool = torch.from_numpy(pool_np.copy()).cuda()
+        mla_dcp_kv_write(dev_src(rows, src_dtype), torch.from_numpy(req).cuda(),
+                         torch.from_numpy(pos).cuda(), torch.from_numpy(np.ascontiguousarray(tab)).cuda(),
+                         begin, N, d_pool, kv_dtype, pool, workspace=ws)
+        torch.cuda.synchronize()
+        slots, bad = okw.dcp_slot_mapping(req, pos, tab, begin, count, N, pool)
+        ref, _ = okw.kv_write(pool_np, kv_dtype, host_f32(rows, src_dtype), slots)
+        assert np.array_equal(d_pool.cpu().numpy(), ref)
+        assert mla_get_device_error(ws) == (MLA_DEVERR_BLOCK_TABLE if bad.any() else 0)
+
+
 def test_write_with_no_owned_tokens_leaves_the_pool_alone():
     T, blocks = 50, 2
     rows = workload.new_token_rows(T, seed=22, dtype="bf16")
@@ -274,3 +315,17 @@ def test_full_size_write_sampled():
     got = pool.view(-1, rb)[torch.from_numpy(slots[sample]).cuda()].cpu().numpy()
     for i in range(sample.size):
         assert np.array_equal(got[i], okw.row_bytes_for(f[i], w["kv_dtype"])), int(sample[i])
+    # the fused call gives the same pool, for all shards at once and shard by shard
+    d_src, d_req, d_pos = dev_src(src, w["src_dtype"]), torch.from_numpy(req).cuda(), torch.from_numpy(posn).cuda()
+    fused = torch.zeros_like(pool)
+    mla_dcp_kv_write(d_src, d_req, d_pos, torch.from_numpy(tables).cuda(), 0, N, fused, w["kv_dtype"],
+                     blocks, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, pool)
+    fused.zero_()
+    for s_ in range(N):
+        mla_dcp_kv_write(d_src, d_req, d_pos, torch.from_numpy(np.ascontiguousarray(tables[s_:s_ + 1])).cuda(),
+                         s_, N, fused, w["kv_dtype"], blocks, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, pool)
+    assert mla_get_device_error(ws) == 0
