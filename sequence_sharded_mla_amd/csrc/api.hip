@@ -72,7 +72,7 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
 
     hipStream_t s = as_stream(stream);
     if (plan.planned) {
-        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, p, plan.target,
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p, plan.target,
                            reinterpret_cast<int32_t*>(w), reinterpret_cast<int32_t*>(w + plan.items_off),
                            reinterpret_cast<int32_t*>(w + plan.row_info_off));
         if ((st = launch_status()) != MLA_OK) return st;

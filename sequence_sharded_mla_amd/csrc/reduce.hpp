@@ -130,40 +130,40 @@ __global__ void __launch_bounds__(256) chunk_combine_kernel(DecodeParams p) {
                              p.out_dtype, head * kLatent, p.lse_out + head, threadIdx.x & 63);
 }
 
-// Inclusive prefix sum over one workgroup of 1024 threads (16 waves); every
-// thread must call it.
-__device__ __forceinline__ int32_t block_scan_1024(int32_t x, int32_t* wave_tot, int32_t& total) {
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+// Exclusive prefix sum of 64-bit values over the plan's workgroup; `total`
+// receives the workgroup sum.  Every thread must call it.
+__device__ __forceinline__ uint64_t block_excl_scan(uint64_t x, uint64_t* wave_tot, uint64_t& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t inc = x;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
+        const uint64_t y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
     }
-    if (lane == 63) wave_tot[wave] = x;
+    if (lane == 63) wave_tot[wave] = inc;
     __syncthreads();
-    int32_t before = 0;
+    uint64_t before = 0;
     total = 0;
-    for (int w = 0; w < 16; ++w) {
-        const int32_t t = wave_tot[w];
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) {
+        const uint64_t t = wave_tot[w];
         if (w < wave) before += t;
         total += t;
     }
     __syncthreads();
-    return x + before;
+    return before + inc - x;
 }
 
-__device__ __forceinline__ int64_t block_sum_1024(int64_t x, int64_t* wave_tot) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    if ((threadIdx.x & 63) == 0) wave_tot[threadIdx.x >> 6] = x;
-    __syncthreads();
-    int64_t t = 0;
-    for (int w = 0; w < 16; ++w) t += wave_tot[w];
-    __syncthreads();
-    return t;
+__device__ __forceinline__ uint64_t block_total(uint64_t x, uint64_t* wave_tot) {
+    uint64_t total;
+    block_excl_scan(x, wave_tot, total);
+    return total;
 }
 
-// Device plan of a dense step (one workgroup of 1024 threads).
+// Device plan of a dense step (one workgroup of kPlanThreads threads).
 //
 // The chunk size T comes from the real total of local tokens (about
 // `target` items, never below kChunkMin).  Row r becomes floor(local / T)
@@ -173,14 +173,19 @@ __device__ __forceinline__ int64_t block_sum_1024(int64_t x, int64_t* wave_tot) 
 // chunks, then the remainder chunks in eight size classes, largest first.
 // row_info[r] = (first partial slot, items of the row); the slots of a split
 // row are consecutive and follow its chunk order.
-__global__ void __launch_bounds__(1024) plan_kernel(DecodeParams p, int32_t target,
-                                                    int32_t* hdr, int32_t* items,
-                                                    int32_t* row_info) {
+//
+// Counts travel packed: per pass of kPlanThreads rows, (full chunks, chunks
+// of split rows) share one 64-bit scan as two 32-bit fields and the eight
+// size classes share two scans as 16-bit fields (at most kPlanThreads per
+// field); over all rows the class counts take 32-bit fields.
+__global__ void __launch_bounds__(kPlanThreads) plan_kernel(DecodeParams p, int32_t target,
+                                                            int32_t* hdr, int32_t* items,
+                                                            int32_t* row_info) {
     constexpr int kBuckets = 8;
-    __shared__ int32_t wave_tot[16];
-    __shared__ int64_t wave_sum64[16];
+    __shared__ uint64_t wave_tot[kPlanWaves];
     const int tid = threadIdx.x;
-    const int64_t cap = int64_t(p.max_blocks) * kBlock;
+    const int32_t cap = int32_t(int64_t(p.max_blocks) * kBlock > INT32_MAX ? INT32_MAX
+                                                                          : int64_t(p.max_blocks) * kBlock);
     auto local_of = [&](int32_t row) -> int32_t {
         RowId r;
         r.row = row;
@@ -188,15 +193,15 @@ __global__ void __launch_bounds__(1024) plan_kernel(DecodeParams p, int32_t targ
         int32_t visible = p.context_lens[r.b] - p.Tq + r.t + 1;
         if (visible < 0) visible = 0;
         const int32_t local = dev_local_len(visible, p.shard_begin + r.s_rel, p.n_shards);
-        return local > cap ? int32_t(cap) : local;
+        return local > cap ? cap : local;
     };
-    int64_t tot = 0;
-    for (int32_t r = tid; r < p.rows; r += 1024) tot += local_of(r);
-    tot = block_sum_1024(tot, wave_sum64);
-    int64_t chunk = (tot + target - 1) / target;
+    uint64_t tot = 0;
+    for (int32_t r = tid; r < p.rows; r += kPlanThreads) tot += uint64_t(local_of(r));
+    tot = block_total(tot, wave_tot);
+    uint64_t chunk = (tot + uint64_t(target) - 1) / uint64_t(target);
     chunk = (chunk + kBlock - 1) / kBlock * kBlock;
-    if (chunk < kChunkMin) chunk = kChunkMin;
-    if (chunk > (int64_t(1) << 30)) chunk = int64_t(1) << 30;
+    if (chunk < uint64_t(kChunkMin)) chunk = kChunkMin;
+    if (chunk > (uint64_t(1) << 30)) chunk = uint64_t(1) << 30;
     const int32_t T = int32_t(chunk);
 
     // shape of row r: full chunks, remainder chunk (0/1), its size class
@@ -210,52 +215,66 @@ __global__ void __launch_bounds__(1024) plan_kernel(DecodeParams p, int32_t targ
         const int32_t left = local - full * T;
         if (left > 0 || local == 0) {
             rem = 1;
-            bucket = int32_t(int64_t(left) * kBuckets / T);
+            bucket = left / (T / kBuckets);  // T is a multiple of 64: floor(8 * left / T)
         }
     };
-    // counts: full chunks, remainder chunks per size class
-    int64_t n_full = 0;
-    int64_t n_b[kBuckets] = {};
-    for (int32_t r0 = 0; r0 < p.rows; r0 += 1024) {
+    // totals: full chunks, and remainder chunks per size class (32-bit fields)
+    uint64_t n_full = 0, n_b01 = 0, n_b23 = 0, n_b45 = 0, n_b67 = 0;
+    for (int32_t r = tid; r < p.rows; r += kPlanThreads) {
         int32_t full, rem, bucket;
-        shape(r0 + tid, full, rem, bucket);
-        n_full += full;
-        if (rem) n_b[bucket] += 1;
+        shape(r, full, rem, bucket);
+        n_full += uint64_t(full);
+        if (rem) {
+            const uint64_t one = uint64_t(1) << (32 * (bucket & 1));
+            if (bucket < 2) n_b01 += one;
+            else if (bucket < 4) n_b23 += one;
+            else if (bucket < 6) n_b45 += one;
+            else n_b67 += one;
+        }
     }
-    n_full = block_sum_1024(n_full, wave_sum64);
-    int64_t off_b[kBuckets];
-    int64_t next = n_full;
+    n_full = block_total(n_full, wave_tot);
+    n_b01 = block_total(n_b01, wave_tot);
+    n_b23 = block_total(n_b23, wave_tot);
+    n_b45 = block_total(n_b45, wave_tot);
+    n_b67 = block_total(n_b67, wave_tot);
+    const uint64_t packs[4] = {n_b01, n_b23, n_b45, n_b67};
+    uint64_t off_b[kBuckets];
+    uint64_t next = n_full;
+#pragma unroll
     for (int b = kBuckets - 1; b >= 0; --b) {
         off_b[b] = next;
-        next += block_sum_1024(n_b[b], wave_sum64);
+        next += (packs[b >> 1] >> (32 * (b & 1))) & 0xffffffffu;
     }
-    const int64_t n_items = next;
+    const uint64_t n_items = next;
 
-    int64_t base_full = 0, base_split = 0;
-    int64_t base_b[kBuckets] = {};
-    for (int32_t r0 = 0; r0 < p.rows; r0 += 1024) {
+    uint64_t base_full = 0, base_split = 0;
+    uint64_t base_b[kBuckets] = {};
+    for (int32_t r0 = 0; r0 < p.rows; r0 += kPlanThreads) {
         const int32_t r = r0 + tid;
         int32_t full, rem, bucket;
         shape(r, full, rem, bucket);
         const int32_t k = full + rem;
         const int32_t ks = k > 1 ? k : 0;
-        int32_t sum_full, sum_ks;
-        const int32_t ex_full = block_scan_1024(full, wave_tot, sum_full) - full;
-        const int32_t ex_ks = block_scan_1024(ks, wave_tot, sum_ks) - ks;
-        int32_t ex_b = 0;
-        for (int b = 0; b < kBuckets; ++b) {
-            const int32_t in = bucket == b ? 1 : 0;
-            int32_t sum_b;
-            const int32_t ex = block_scan_1024(in, wave_tot, sum_b) - in;
-            if (in) ex_b = int32_t(off_b[b] + base_b[b] + ex);
-            base_b[b] += sum_b;
-        }
+        uint64_t tot_fk;
+        const uint64_t ex_fk = block_excl_scan(uint64_t(uint32_t(full)) | (uint64_t(uint32_t(ks)) << 32),
+                                               wave_tot, tot_fk);
+        const uint64_t onehot = rem ? uint64_t(1) << (16 * (bucket & 3)) : 0;
+        uint64_t tot_lo, tot_hi;
+        const uint64_t ex_lo = block_excl_scan(bucket < 4 ? onehot : 0, wave_tot, tot_lo);
+        const uint64_t ex_hi = block_excl_scan(bucket >= 4 ? onehot : 0, wave_tot, tot_hi);
         if (r < p.rows) {
-            const int64_t slot0 = k > 1 ? base_split + ex_ks : -1;
+            const uint64_t ex_full = ex_fk & 0xffffffffu, ex_ks = ex_fk >> 32;
+            uint64_t ex_b = 0;
+#pragma unroll
+            for (int b = 0; b < kBuckets; ++b) {
+                const uint64_t field = ((b < 4 ? ex_lo : ex_hi) >> (16 * (b & 3))) & 0xffffu;
+                if (bucket == b) ex_b = off_b[b] + base_b[b] + field;
+            }
+            const int64_t slot0 = k > 1 ? int64_t(base_split + ex_ks) : -1;
             row_info[2 * size_t(r)] = int32_t(slot0);
             row_info[2 * size_t(r) + 1] = k;
             for (int32_t c = 0; c < k; ++c) {
-                const int64_t pos = c < full ? base_full + ex_full + c : ex_b;
+                const uint64_t pos = c < full ? base_full + ex_full + uint64_t(c) : ex_b;
                 int32_t* it = items + 4 * size_t(pos);
                 it[0] = r;
                 it[1] = c;
@@ -263,8 +282,11 @@ __global__ void __launch_bounds__(1024) plan_kernel(DecodeParams p, int32_t targ
                 it[3] = 0;
             }
         }
-        base_full += sum_full;
-        base_split += sum_ks;
+        base_full += tot_fk & 0xffffffffu;
+        base_split += tot_fk >> 32;
+#pragma unroll
+        for (int b = 0; b < kBuckets; ++b)
+            base_b[b] += ((b < 4 ? tot_lo : tot_hi) >> (16 * (b & 3))) & 0xffffu;
     }
     if (tid == 0) {
         hdr[1] = int32_t(n_items);
