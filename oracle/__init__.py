@@ -32,6 +32,11 @@ What it computes, with the page each part follows:
   correctness blocker visible") and the row it receives in the cache's
   storage format, with the fp8 codes chosen by a per-group scale and
   round-to-nearest-even (a reading; the pages give no quantiser).
+* Top-K selection of the sparse indices from indexer scores over each query
+  token's causal prefix, per shard and merged across shards ("GLM-5.2 vLLM
+  Decode Context Parallelism", section "Understand the cache-copy
+  opportunity": top-K of 2,048; "How vLLM Serves GLM-5.3 with Million-Token
+  Contexts on 16 H200s", section "Why conventional TP and DP fall short").
 
 Every function states the passage it follows.  Where the pages leave a step
 open, the reading taken is stated at the function.
@@ -45,4 +50,4 @@ brute-force enumeration for the integer steps, and the tables the pages
 print (copy geometry, head envelope, per-token byte counts).
 """
 
-from . import codecs, sharding, attention, capacity, decode, kv_write  # noqa: F401
+from . import codecs, sharding, attention, capacity, decode, kv_write, topk  # noqa: F401
