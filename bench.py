@@ -32,6 +32,8 @@ KERNEL_SOURCES = ["decode_valu.hpp", "decode_mfma.hpp", "decode_fp8.hpp", "mfma_
                   "params.hpp", "api.hip",
                   "reduce.hpp", "plan.hpp", "host.cpp"]
 WRITE_SOURCES = ["kv_write.hpp", "common.hpp", "api.hip"]
+TOPK_SOURCES = ["topk.hpp", "common.hpp", "api.hip"]
+TOPK_METRIC = "DCP top-K index selection: achieved HBM GB/s (% of peak) and rows/s, per-shard top-2048 + merge"
 WRITE_METRIC = "DCP KV cache write: achieved HBM GB/s (% of peak) and tokens/s, 1M tokens over 8 shards"
 
 
@@ -153,6 +155,112 @@ def time_launches(fn, K, stream):
     return np.array([a.elapsed_time(b) for a, b in ev])
 
 
+def topk_cpu_baseline(scores, lens, w, budget_s=10.0):
+    """Time the oracle's per-shard selection + merge on whole rows."""
+    from oracle import topk as otk
+    B, Tq, K, N = w["batch"], w["q_len"], w["topk"], w["n_shards"]
+    done, t0 = 0, time.perf_counter()
+    while done < B and (time.perf_counter() - t0) < budget_s:
+        sl = slice(done, done + 1)
+        parts = [otk.local_topk(scores[sl], lens[sl], Tq, K, s, N) for s in range(N)]
+        otk.merge_topk(np.stack([p.reshape(Tq, K) for p, _ in parts]),
+                       np.stack([c.reshape(Tq, K) for _, c in parts]), K)
+        done += 1
+    dt = time.perf_counter() - t0
+    score_bytes = done * Tq * w["context"] * 4
+    return {"value": round(score_bytes / dt / 1e9, 6), "unit": "GB/s",
+            "rows_per_s": round(done * Tq / dt, 2), "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {B} requests ({done * Tq} rows, all {N} shards + merge), {dt:.1f} s"}
+
+
+def run_topk(args):
+    """Top-K selection for every query token of the sparse workload: each
+    shard's local top-K (all shards in one launch), then the merge."""
+    import torch
+    import workload
+    from sequence_sharded_mla_amd import layout, mla_topk_local, mla_topk_merge
+    name = "topk_select_262k"
+    w = workload.SELECT_SPECS[name]
+    B, Tq, L, K, N = w["batch"], w["q_len"], w["context"], w["topk"], w["n_shards"]
+    log(f"bench: generating {name}")
+    scores = workload.indexer_scores(B, Tq, L, seed=w["seed"])
+    lens = np.full(B, L, dtype=np.int32)
+    sc_sh = layout.shard_scores(scores, N)
+    d_sc = torch.from_numpy(sc_sh).cuda()
+    d_lens = torch.from_numpy(lens).cuda()
+    rows = B * Tq
+    ci = torch.empty((N, B, Tq, K), dtype=torch.int32, device="cuda")
+    cs = torch.empty((N, B, Tq, K), dtype=torch.float32, device="cuda")
+    out = torch.empty((rows, K), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def local():
+        mla_topk_local(d_sc, d_lens, K, 0, N, ci, cs)
+
+    def merge():
+        mla_topk_merge(ci.view(N, rows, K), cs.view(N, rows, K), K, out)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        local()
+        merge()
+    torch.cuda.synchronize()
+    K_steps = args.steps
+    log(f"bench: timing {K_steps} steps")
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K_steps)]
+    t0 = time.perf_counter()
+    for a, b, c in ev:
+        a.record(stream)
+        local()
+        b.record(stream)
+        merge()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_loc = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    t_mer = np.array([b.elapsed_time(c) for _, b, c in ev])
+    ms_step = wall * 1e3 / K_steps
+    # every owned score read once; candidates written once and read once; result written once
+    local_bytes = B * Tq * L * 4 + B * 4 + N * rows * K * 8
+    merge_bytes = N * rows * K * 8 + rows * K * 4
+    step_bytes = local_bytes + merge_bytes
+    loc_ms = float(np.mean(t_loc))
+    achieved = local_bytes / (loc_ms * 1e-3) / 1e9
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    khash = kernel_hash(TOPK_SOURCES)
+    rec = {
+        "metric": TOPK_METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) indexer scores)",
+        "config": {"workload": name, "batch": B, "q_len": Tq, "context": L, "topk": K, "n_shards": N},
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "rows_per_s": round(rows / (ms_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "kernels_ms": {"local_topk": round(loc_ms, 4), "merge_topk": round(float(np.mean(t_mer)), 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for(name, khash),
+                     "kernel": "local_topk_kernel (all shards, one launch)",
+                     "algorithmic_bytes_per_launch": int(local_bytes)},
+        "kernel_hash": khash,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host")
+        rec["cpu_baseline"] = topk_cpu_baseline(scores, lens, w, args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
 def run_kv_write(args):
     """Cache write of one request's 1M new tokens, dealt over 8 shards held in
     one pool: the fused owner-slot + quantise-and-store call (one launch)."""
@@ -260,6 +368,8 @@ def main():
     ap.add_argument("--kv-write", action="store_true",
                     help="time the cache write (owner slot mapping + quantise-and-store) instead "
                          "of the decode step")
+    ap.add_argument("--topk", action="store_true",
+                    help="time the top-K index selection (per-shard local top-K + merge)")
     ap.add_argument("--no-extras", action="store_true",
                     help="with --kv-write: time only the fused all-shard call (for profiling)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -282,6 +392,9 @@ def main():
         return
     if args.kv_write:
         run_kv_write(args)
+        return
+    if args.topk:
+        run_topk(args)
         return
     import workload
     from sequence_sharded_mla_amd import layout, mla_get_device_error

@@ -89,6 +89,7 @@ extern "C" {
 #define MLA_DEVERR_BLOCK_TABLE 1u /* table too narrow, or block id out of pool */
 #define MLA_DEVERR_INDEX 2u       /* top-K index beyond the causal prefix      */
 #define MLA_DEVERR_SLOT 4u        /* cache-write slot at or past the pool end  */
+#define MLA_DEVERR_SCORES 8u      /* score row shorter than the visible prefix */
 
 /* Shape of one decode step.  Fixed by this build: kv_lora_rank = 512,
  * rope_dim = 64, block_size = 64; num_heads in {16, 32, 64, 128} (the query
@@ -249,6 +250,44 @@ int32_t mla_dcp_kv_write(const void* kv_new, int32_t src_dtype, const int32_t* r
                          int32_t batch, int32_t max_blocks, int32_t shard_begin, int32_t shard_count,
                          int32_t n_shards, int32_t kv_dtype, void* kv_pool, int64_t pool_blocks,
                          void* workspace, void* stream);
+
+/* Local top-K of the sparse indices on shards shard_begin .. shard_begin +
+ * shard_count - 1: for every request b and query token t, the topk best
+ * positions the shard owns in the token's causal prefix (positions 0 ..
+ * L_b - Tq + t) by indexer score ("GLM-5.2 vLLM Decode Context Parallelism",
+ * section "Understand the cache-copy opportunity": sparse index top-K;
+ * "How vLLM Serves GLM-5.3 with Million-Token Contexts on 16 H200s", section
+ * "Why conventional TP and DP fall short": the indexer scores earlier
+ * tokens, sparse attention selects a fixed set).  Order: larger score first,
+ * equal scores by lower position (+0 and -0 equal); the selection is unique.
+ *   scores      [shard_count][B][Tq][row_stride] f32: entry j of shard s is the
+ *               score of global position j * n_shards + s (what a DCP rank
+ *               holds for its own tokens); finite or -inf
+ *   cand_idx    [shard_count][B][Tq][topk] int32 GLOBAL positions, ascending,
+ *               padded with -1 when the shard owns fewer than topk
+ *   cand_score  [shard_count][B][Tq][topk] f32, the scores of cand_idx (-0 as
+ *               +0; -inf
+ *               for padding)
+ *   workspace   NULL or a buffer whose first 32-bit word is the error word:
+ *               a row_stride shorter than a shard's visible prefix sets
+ *               MLA_DEVERR_SCORES and only the first row_stride entries count
+ * 1 <= row_stride <= 2^19, topk >= 1, scores 4-byte aligned.  Bit-exact. */
+int32_t mla_topk_local(const float* scores, int64_t row_stride, const int32_t* context_lens,
+                       int32_t batch, int32_t q_len, int32_t topk, int32_t shard_begin,
+                       int32_t shard_count, int32_t n_shards, int32_t* cand_idx, float* cand_score,
+                       void* workspace, void* stream);
+
+/* Merge of candidate lists into the global top-K: for each row, the topk
+ * best of the union of the n_lists lists (same order as mla_topk_local), as
+ * ascending positions padded with -1.  Every global top-K position is in its
+ * owner's local top-K, so merging the shards' mla_topk_local lists gives the
+ * selection over the whole prefix.
+ *   cand_idx, cand_score  [n_lists][rows][cand_k] (entries with index < 0 are
+ *                         padding; positions must be distinct within a row)
+ *   topk_idx              [rows][topk] int32 (the sparse decode's top-K input)
+ * 1 <= n_lists, 1 <= topk <= 8192, n_lists * cand_k <= 2^18. */
+int32_t mla_topk_merge(const int32_t* cand_idx, const float* cand_score, int32_t n_lists, int64_t rows,
+                       int32_t cand_k, int32_t topk, int32_t* topk_idx, void* stream);
 
 /* Read the device error word of a workspace: waits for `stream`, then copies
  * the word to *code_out (0 = no error; else MLA_DEVERR_* bits). */

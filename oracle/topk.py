@@ -19,7 +19,8 @@ Readings (the pages give no selection rule beyond "top-K"):
   position first, so the selected set is unique;
 * a list is returned as its positions in ascending order, padded with -1
   when fewer than K positions exist (scores of padded entries are -inf);
-* scores are finite float32 or -inf.
+* scores are finite float32 or -inf; +0 and -0 are one value, and a
+  candidate list returns that value as +0.
 """
 
 import numpy as np
@@ -75,6 +76,8 @@ def local_topk(scores, context_lens, q_len, k, shard, n_shards):
             n = visible(context_lens[b], q_len, t)
             owned = np.arange(shard, n, n_shards)
             pos[b, t], sc[b, t] = select(owned, scores[b, t, owned], k)
+    # -0 and +0 are one value; a candidate's score is returned as +0
+    sc[sc == 0] = 0.0
     return pos, sc
 
 

@@ -13,7 +13,7 @@ import torch
 
 from . import _lib
 from ._lib import (MLA_BF16, MLA_F32, MLA_FP8_DS, MLA_DEVERR_BLOCK_TABLE,  # noqa: F401
-                   MLA_DEVERR_INDEX, MLA_DEVERR_SLOT, MLADecodeDesc)
+                   MLA_DEVERR_INDEX, MLA_DEVERR_SLOT, MLA_DEVERR_SCORES, MLADecodeDesc)
 
 DTYPE_CODES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8_ds": MLA_FP8_DS}
 LATENT = 512
@@ -150,6 +150,26 @@ def mla_dcp_kv_write(kv_new, req_idx, positions, block_tables, shard_begin, n_sh
         _ptr(block_tables), batch, max_blocks, shard_begin, shard_count, n_shards,
         DTYPE_CODES.get(kv_dtype, kv_dtype), _ptr(kv_pool), pool_blocks, _ptr(workspace),
         _stream(stream)), "mla_dcp_kv_write")
+
+
+def mla_topk_local(scores, context_lens, topk, shard_begin, n_shards, cand_idx, cand_score,
+                   workspace=None, stream=None):
+    """scores [shard_count][B][Tq][stride] f32 -> cand_idx / cand_score [shard_count][B][Tq][topk]."""
+    shard_count, batch, q_len, stride = scores.shape
+    _check(_lib.load().mla_topk_local(
+        _ptr(scores), stride, _ptr(context_lens), batch, q_len, topk, shard_begin, shard_count,
+        n_shards, _ptr(cand_idx), _ptr(cand_score), _ptr(workspace), _stream(stream)),
+        "mla_topk_local")
+
+
+def mla_topk_merge(cand_idx, cand_score, topk, topk_idx, stream=None):
+    """cand_* [n_lists][rows][cand_k] -> topk_idx [rows][topk]."""
+    n_lists = cand_idx.shape[0]
+    cand_k = cand_idx.shape[-1]
+    rows = cand_idx.numel() // (n_lists * cand_k)
+    _check(_lib.load().mla_topk_merge(
+        _ptr(cand_idx), _ptr(cand_score), n_lists, rows, cand_k, topk, _ptr(topk_idx),
+        _stream(stream)), "mla_topk_merge")
 
 
 def mla_get_device_error(workspace, stream=None):

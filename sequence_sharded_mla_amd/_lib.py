@@ -26,6 +26,7 @@ MLA_FP8_DS = 2
 MLA_DEVERR_BLOCK_TABLE = 1
 MLA_DEVERR_INDEX = 2
 MLA_DEVERR_SLOT = 4
+MLA_DEVERR_SCORES = 8
 
 
 class MLADecodeDesc(ctypes.Structure):
@@ -68,6 +69,8 @@ SIGNATURES = {
     "mla_kv_write": (_i32, [_vp, _i32, _i64, _vp, _i32, _vp, _i64, _vp, _vp]),
     "mla_dcp_kv_write": (_i32, [_vp, _i32, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _vp, _i64, _vp, _vp]),
+    "mla_topk_local": (_i32, [_vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "mla_topk_merge": (_i32, [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp]),
     "mla_get_device_error": (_i32, [_vp, ctypes.POINTER(_i32), _vp]),
     "mla_clear_device_error": (_i32, [_vp, _vp]),
 }

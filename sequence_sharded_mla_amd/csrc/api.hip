@@ -7,6 +7,7 @@
 #include "decode_mfma.hpp"
 #include "decode_valu.hpp"
 #include "kv_write.hpp"
+#include "topk.hpp"
 #include "params.hpp"
 #include "plan.hpp"
 #include "reduce.hpp"
@@ -317,6 +318,71 @@ int32_t mla_dcp_kv_write(const void* kv_new, int32_t src_dtype, const int32_t* r
     const int32_t per_wave = (n_shards + shard_count - 1) / shard_count;
     return mla::launch_write(p, kv_new, src_dtype, n_tokens, kv_dtype, kv_pool, pool_blocks, workspace,
                              per_wave > 8 ? 8 : per_wave, true, stream);
+}
+
+int32_t mla_topk_local(const float* scores, int64_t row_stride, const int32_t* context_lens,
+                       int32_t batch, int32_t q_len, int32_t topk, int32_t shard_begin,
+                       int32_t shard_count, int32_t n_shards, int32_t* cand_idx, float* cand_score,
+                       void* workspace, void* stream) {
+    using namespace mla::topk;
+    if (batch < 0 || q_len < 1 || topk < 1 || row_stride < 1 || row_stride > kMaxLocal)
+        return MLA_ERR_SHAPE;
+    if (n_shards < 1 || shard_begin < 0 || shard_count < 1 || shard_begin + shard_count > n_shards)
+        return MLA_ERR_SHARD;
+    const int64_t rows = int64_t(shard_count) * batch * q_len;
+    if (rows > INT32_MAX || rows * int64_t(topk) > (int64_t(1) << 40)) return MLA_ERR_SHAPE;
+    if (rows == 0) return MLA_OK;
+    if (!scores || !context_lens || !cand_idx || !cand_score) return MLA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(scores) & 3u) || (reinterpret_cast<uintptr_t>(cand_idx) & 3u) ||
+        (reinterpret_cast<uintptr_t>(cand_score) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+        return MLA_ERR_ALIGN;
+    LocalParams p{};
+    p.scores = scores;
+    p.context_lens = context_lens;
+    p.out_idx = cand_idx;
+    p.out_score = cand_score;
+    p.err = static_cast<uint32_t*>(workspace);
+    p.stride = row_stride;
+    p.B = batch;
+    p.Tq = q_len;
+    p.K = topk;
+    p.shard_begin = shard_begin;
+    p.n_shards = n_shards;
+    const int32_t words = int32_t((row_stride + 31) / 32);
+    hipLaunchKernelGGL(local_topk_kernel, dim3(uint32_t(rows)), dim3(kThreads), size_t(words) * 8,
+                       mla::as_stream(stream), p, words);
+    return mla::launch_status();
+}
+
+int32_t mla_topk_merge(const int32_t* cand_idx, const float* cand_score, int32_t n_lists, int64_t rows,
+                       int32_t cand_k, int32_t topk, int32_t* topk_idx, void* stream) {
+    using namespace mla::topk;
+    if (n_lists < 1 || rows < 0 || cand_k < 1 || topk < 1 || topk > kMaxMergeK ||
+        int64_t(n_lists) * cand_k > kMaxCand || rows > INT32_MAX)
+        return MLA_ERR_SHAPE;
+    if (rows == 0) return MLA_OK;
+    if (!cand_idx || !cand_score || !topk_idx) return MLA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cand_idx) & 3u) || (reinterpret_cast<uintptr_t>(cand_score) & 3u) ||
+        (reinterpret_cast<uintptr_t>(topk_idx) & 3u))
+        return MLA_ERR_ALIGN;
+    MergeParams p{};
+    p.cand_idx = cand_idx;
+    p.cand_score = cand_score;
+    p.out_idx = topk_idx;
+    p.rows = rows;
+    p.n_lists = n_lists;
+    p.k_in = cand_k;
+    p.K = topk;
+    const int32_t words = int32_t((int64_t(n_lists) * cand_k + 31) / 32);
+    int32_t pw = 1;
+    while (pw < topk) pw <<= 1;
+    if (int64_t(n_lists) * cand_k <= kStage / 2 && topk <= kStageK)
+        hipLaunchKernelGGL(merge_topk_staged_kernel, dim3(uint32_t(rows)), dim3(kThreads), 0,
+                           mla::as_stream(stream), p);
+    else
+        hipLaunchKernelGGL(merge_topk_kernel, dim3(uint32_t(rows)), dim3(kThreads),
+                           size_t(words) * 4 + size_t(pw) * 4, mla::as_stream(stream), p, words);
+    return mla::launch_status();
 }
 
 int32_t mla_get_device_error(const void* workspace, int32_t* code_out, void* stream) {

@@ -1,0 +1,627 @@
+// Top-K selection of sparse-attention indices, per shard and merged (gfx950).
+//
+// A query token attends the K best positions of its causal prefix by
+// indexer score ("GLM-5.2 vLLM Decode Context Parallelism", section
+// "Understand the cache-copy opportunity": top-K of 2,048; "How vLLM Serves
+// GLM-5.3 with Million-Token Contexts on 16 H200s", section "Why
+// conventional TP and DP fall short": the indexer scores earlier tokens and
+// sparse attention selects a fixed set).  With the cache sharded
+// round-robin, a shard holds the scores of its own positions: it selects its
+// local top-K, and the top-K of the union of the shards' lists is the global
+// top-K.
+//
+// Order: larger score first; equal scores (+0 and -0 are one value) by lower
+// position.  Every element therefore has a distinct 64-bit key
+//   key = order-preserving bits of the score << 32 | ~id
+// (id = local index or global position, both increasing with position), and
+// the K elements with the largest keys are the selection.  Lists are written
+// as ascending positions padded with -1 (scores of padded entries -inf).
+//
+// One workgroup per row.  The K-th key is found digit by digit from the top
+// (12, 12, 8, 12, 12, 8 bits): a histogram of the elements still tied with
+// the prefix found so far (LDS atomics), then a suffix scan picks the digit
+// holding the K-th key.  As soon as the tied group is small enough
+// (<= kCand), one more pass over the row sets a bit for every element above
+// the group and copies the group into LDS, where a bitonic sort by key
+// settles it.  The set bits, read in index order, give the output; a row
+// usually needs two passes over its scores (one from HBM, one from cache).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla_dcp.h"
+#include "common.hpp"
+
+namespace mla {
+namespace topk {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 512;
+constexpr int kWavesT = kThreads / 64;
+constexpr int kBins = 4096;       // 12-bit digits
+constexpr int kCand = 2048;       // tied group resolved in LDS (a power of two)
+constexpr int kSel = 2048;        // local rows with K <= kSel list their selection in LDS
+constexpr int kMaxMergeK = 8192;  // output list sorted in LDS by the merge
+constexpr int64_t kMaxLocal = int64_t(1) << 19;   // local positions per row (64 KB bitmap in LDS)
+constexpr int64_t kMaxCand = int64_t(1) << 18;    // candidates per merged row (32 KB bitmap)
+constexpr int kStage = 32768;     // merge rows of up to kStage / 2 candidates are read once into LDS
+constexpr int kStageK = kCand;    // largest K the staged merge sorts in the tied-group space
+
+struct LocalParams {
+    const float* scores;     // [shard_count][B][Tq][stride]
+    const int32_t* context_lens;
+    int32_t* out_idx;        // [shard_count][B][Tq][K]
+    float* out_score;        // [shard_count][B][Tq][K]
+    uint32_t* err;           // may be null
+    int64_t stride;
+    int32_t B, Tq, K, shard_begin, n_shards;
+};
+
+struct MergeParams {
+    const int32_t* cand_idx;  // [n_lists][rows][k_in]
+    const float* cand_score;
+    int32_t* out_idx;         // [rows][K]
+    int64_t rows;
+    int32_t n_lists, k_in, K;
+};
+
+// Order-preserving bits of a float (larger float -> larger unsigned value);
+// -0 and +0 map to the same value.
+__device__ __forceinline__ uint32_t score_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) == 0) u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t make_key(float score, uint32_t id) {
+    return (uint64_t(score_bits(score)) << 32) | uint64_t(~id);
+}
+
+// Digits from the top of the 64-bit key: (shift, width).
+__device__ __forceinline__ int digit_shift(int pass) {
+    constexpr int kShift[6] = {52, 40, 32, 20, 8, 0};
+    return kShift[pass];
+}
+__device__ __forceinline__ int digit_width(int pass) { return (pass % 3 == 2) ? 8 : 12; }
+
+// The selected elements of a row (key and index, in no particular order).
+struct SelList {
+    uint64_t key[kSel];
+    uint32_t idx[kSel];
+    uint32_t n;
+};
+
+struct SelectShared {
+    // the histogram serves the digit passes, the tied group the last pass
+    union {
+        uint32_t hist[kBins];
+        struct {
+            uint64_t cand_key[kCand];
+            uint32_t cand_idx[kCand];
+        };
+    };
+    uint64_t prefix;         // fixed top bits of the K-th key
+    uint64_t mask;           // which bits are fixed
+    uint32_t need;           // elements still to take from the tied group
+    uint32_t tied;           // size of the tied group
+    uint32_t n_cand;
+    uint32_t scan[kWavesT];
+};
+
+// Inclusive scan helpers over the workgroup (kThreads threads).
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t x, uint32_t* wave_tot, uint32_t& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) wave_tot[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesT; ++w) {
+        const uint32_t t = wave_tot[w];
+        if (w < wave) before += t;
+        total += t;
+    }
+    __syncthreads();
+    return before + inc - x;
+}
+
+// Slot of this lane among the lanes of its wave that append (pred), taken
+// from `counter` with one atomic per wave.  Every active lane must call it.
+__device__ __forceinline__ uint32_t wave_append(uint32_t* counter, bool pred) {
+    const uint64_t m = __ballot(pred);
+    if (!m) return 0;
+    const int leader = __builtin_ctzll(m);
+    uint32_t base = 0;
+    if ((threadIdx.x & 63) == leader) base = atomicAdd(counter, uint32_t(__popcll(m)));
+    base = __shfl(base, leader);
+    return base + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+}
+
+// Finds the digit holding the need-th largest key among the histogram's
+// bins (nbins <= kBins), updates prefix/mask/need/tied.  All threads call.
+__device__ __forceinline__ void pick_digit(SelectShared& sh, int nbins, int shift) {
+    // each thread sums a contiguous run of bins, counted from the top bin down
+    constexpr int kPer = kBins / kThreads;  // 8
+    const int per = nbins / kThreads > 0 ? nbins / kThreads : 1;
+    const int active = nbins / per;  // threads holding bins
+    uint32_t mine = 0;
+    const int t = threadIdx.x;
+    if (t < active) {
+        for (int j = 0; j < per && j < kPer; ++j) mine += sh.hist[nbins - 1 - (t * per + j)];
+    }
+    const uint32_t need = sh.need;  // read before the scan's barriers: one thread rewrites it
+    uint32_t total;
+    const uint32_t before = block_excl_scan_u32(mine, sh.scan, total);  // count of larger bins
+    if (t < active && before < need && need <= before + mine) {
+        uint32_t above = before;
+        for (int j = 0; j < per; ++j) {
+            const int bin = nbins - 1 - (t * per + j);
+            const uint32_t c = sh.hist[bin];
+            if (need <= above + c) {
+                sh.prefix |= uint64_t(bin) << shift;
+                sh.mask |= uint64_t(nbins - 1) << shift;
+                sh.need = need - above;
+                sh.tied = c;
+                break;
+            }
+            above += c;
+        }
+    }
+    __syncthreads();
+}
+
+// Bitonic sort of sh.cand_key / cand_idx [0, n) descending by key, padding
+// up to the next power of two with key 0 (below every real key, whose score
+// bits are non-zero).
+__device__ __forceinline__ void sort_candidates_desc(SelectShared& sh, uint32_t n) {
+    uint32_t p = 1;
+    while (p < n) p <<= 1;
+    for (uint32_t i = n + threadIdx.x; i < p; i += kThreads) {
+        sh.cand_key[i] = 0;
+        sh.cand_idx[i] = 0;
+    }
+    __syncthreads();
+    for (uint32_t size = 2; size <= p; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t i = threadIdx.x; i < p / 2; i += kThreads) {
+                const uint32_t lo = 2 * i - (i & (stride - 1));
+                const uint32_t hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t a = sh.cand_key[lo], b = sh.cand_key[hi];
+                if ((a < b) == desc) {
+                    sh.cand_key[lo] = b;
+                    sh.cand_key[hi] = a;
+                    const uint32_t ia = sh.cand_idx[lo];
+                    sh.cand_idx[lo] = sh.cand_idx[hi];
+                    sh.cand_idx[hi] = ia;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Calls f(i, key) for every element i < n whose key is not 0 (0 marks an
+// invalid element; every real key is larger).  A source loads Src::V
+// consecutive elements at once; each thread requests U such loads before
+// using the first, so U loads per lane are in flight.
+template <int U, typename Src, typename F>
+__device__ __forceinline__ void for_each_key(const Src& src, int64_t n, F f) {
+    constexpr int V = Src::V;
+    const int64_t groups = (n + V - 1) / V;
+    for (int64_t g0 = threadIdx.x; g0 < groups; g0 += int64_t(kThreads) * U) {
+        uint64_t k[U][V];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + int64_t(u) * kThreads;
+            if (g < groups) src.keys(g, n, k[u]);
+            else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) k[u][v] = 0;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                if (k[u][v]) f((g0 + int64_t(u) * kThreads) * V + v, k[u][v]);
+    }
+}
+
+// COLLECT: also list the selected elements in *sel (K <= kSel).
+template <int U, bool COLLECT, typename Src>
+__device__ void select_into_bitmap(SelectShared& sh, const Src& src, int64_t n, uint32_t K,
+                                   uint32_t* bits, SelList* sel = nullptr) {
+    if (threadIdx.x == 0) {
+        sh.prefix = 0;
+        sh.mask = 0;
+        sh.need = K;
+        sh.tied = uint32_t(n);
+        sh.n_cand = 0;
+        if (COLLECT) sel->n = 0;
+    }
+    __syncthreads();
+    for (int pass = 0; pass < 6; ++pass) {
+        if (sh.tied <= uint32_t(kCand) || sh.tied == sh.need) break;
+        const int shift = digit_shift(pass);
+        const int nbins = 1 << digit_width(pass);
+        for (int i = threadIdx.x; i < nbins; i += kThreads) sh.hist[i] = 0;
+        __syncthreads();
+        const uint64_t prefix = sh.prefix, mask = sh.mask;
+        for_each_key<U>(src, n, [&](int64_t, uint64_t k) {
+            if ((k & mask) == prefix) atomicAdd(&sh.hist[uint32_t(k >> shift) & uint32_t(nbins - 1)], 1u);
+        });
+        __syncthreads();
+        pick_digit(sh, nbins, shift);
+    }
+    // one pass: elements above the tied group are selected; the group goes
+    // to LDS unless all of it is taken
+    const uint64_t prefix = sh.prefix, mask = sh.mask;
+    const bool take_all = sh.tied == sh.need;
+    constexpr int V = Src::V;
+    const int64_t groups = (n + V - 1) / V;
+    for (int64_t g0 = threadIdx.x; g0 < groups; g0 += int64_t(kThreads) * U) {
+        uint64_t k[U][V];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + int64_t(u) * kThreads;
+            if (g < groups) src.keys(g, n, k[u]);
+            else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) k[u][v] = 0;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int64_t i = (g0 + int64_t(u) * kThreads) * V + v;
+                const uint64_t kk = k[u][v];
+                const uint64_t top = kk & mask;
+                const bool is_sel = kk && (top > prefix || (top == prefix && take_all));
+                const bool tie = kk && top == prefix && !take_all;
+                if (is_sel) atomicOr(&bits[i >> 5], 1u << (i & 31));
+                if (COLLECT) {
+                    const uint32_t at = wave_append(&sel->n, is_sel);
+                    if (is_sel) {
+                        sel->key[at] = kk;
+                        sel->idx[at] = uint32_t(i);
+                    }
+                }
+                const uint32_t slot = wave_append(&sh.n_cand, tie);
+                if (tie) {
+                    sh.cand_key[slot] = kk;
+                    sh.cand_idx[slot] = uint32_t(i);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (!take_all) {
+        const uint32_t nc = sh.n_cand;
+        const uint32_t ns = COLLECT ? sel->n : 0;
+        sort_candidates_desc(sh, nc);
+        for (uint32_t j = threadIdx.x; j < sh.need; j += kThreads) {
+            const uint32_t i = sh.cand_idx[j];
+            atomicOr(&bits[i >> 5], 1u << (i & 31));
+            if (COLLECT) {
+                sel->key[ns + j] = sh.cand_key[j];
+                sel->idx[ns + j] = i;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// A score row read one float per element.
+struct LocalSrc {
+    static constexpr int V = 1;
+    const float* row;
+    __device__ void keys(int64_t g, int64_t, uint64_t (&k)[V]) const { k[0] = make_key(row[g], uint32_t(g)); }
+};
+
+// A score row read 16 bytes (four elements) per load; the row is 16-byte
+// aligned and readable up to n rounded up to four.
+struct LocalSrc4 {
+    static constexpr int V = 4;
+    const float* row;
+    __device__ void keys(int64_t g, int64_t n, uint64_t (&k)[V]) const {
+        const f32x4_t x = reinterpret_cast<const f32x4_t*>(row)[g];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int64_t i = g * V + v;
+            k[v] = i < n ? make_key(x[v], uint32_t(i)) : 0;
+        }
+    }
+};
+
+// A candidate score as returned: the stored score, with -0 written as +0
+// (the two are one value for the selection).
+__device__ __forceinline__ float canon(float x) { return x == 0.f ? 0.f : x; }
+
+// The score a key was made from (canonical: -0 comes back as +0).
+__device__ __forceinline__ float score_of(uint64_t key) {
+    const uint32_t b = uint32_t(key >> 32);
+    return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
+
+// Local top-K of one (shard, request, query token) row.  Dynamic LDS: the
+// bitmap (one bit per local position of the longest row of the launch) and
+// the running count of set bits before each bitmap word.
+__global__ void __launch_bounds__(kThreads) local_topk_kernel(LocalParams p, int32_t bitmap_words) {
+    __shared__ SelectShared sh;
+    __shared__ SelList sel;
+    extern __shared__ uint32_t dyn[];
+    uint32_t* bits = dyn;
+    uint32_t* wprefix = dyn + bitmap_words;
+    const int32_t row = blockIdx.x;  // (s_rel, b, t)
+    const int32_t t = row % p.Tq;
+    const int32_t b = (row / p.Tq) % p.B;
+    const int32_t s_rel = row / (p.Tq * p.B);
+    const int32_t s = p.shard_begin + s_rel;
+    int32_t vis = p.context_lens[b] - p.Tq + t + 1;
+    if (vis < 0) vis = 0;
+    int64_t n = dev_local_len(vis, s, p.n_shards);
+    if (n > p.stride) {  // the score row is shorter than the shard's visible prefix
+        if (threadIdx.x == 0 && p.err) raise_error(p.err, MLA_DEVERR_SCORES);
+        n = p.stride;
+    }
+    const float* scores = p.scores + size_t(row) * p.stride;
+    int32_t* out_i = p.out_idx + size_t(row) * p.K;
+    float* out_s = p.out_score + size_t(row) * p.K;
+    if (n <= p.K) {  // every owned position is kept, in order
+        for (int64_t j = threadIdx.x; j < p.K; j += kThreads) {
+            out_i[j] = j < n ? int32_t(j * p.n_shards + s) : -1;
+            out_s[j] = j < n ? canon(scores[j]) : -INFINITY;
+        }
+        return;
+    }
+    const int32_t words = int32_t((n + 31) >> 5);
+    for (int i = threadIdx.x; i < words; i += kThreads) bits[i] = 0;
+    __syncthreads();
+    const int per = (words + kThreads - 1) / kThreads;
+    const int w0 = threadIdx.x * per;
+    const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (p.stride & 3) == 0;
+    if (p.K <= kSel) {
+        if (vec)
+            select_into_bitmap<4, true>(sh, LocalSrc4{scores}, n, uint32_t(p.K), bits, &sel);
+        else
+            select_into_bitmap<16, true>(sh, LocalSrc{scores}, n, uint32_t(p.K), bits, &sel);
+        // output slot of a kept element = kept elements before it
+        uint32_t cnt = 0;
+        for (int w = w0; w < w0 + per && w < words; ++w) cnt += __popc(bits[w]);
+        uint32_t total;
+        uint32_t run = block_excl_scan_u32(cnt, sh.scan, total);
+        for (int w = w0; w < w0 + per && w < words; ++w) {
+            wprefix[w] = run;
+            run += __popc(bits[w]);
+        }
+        __syncthreads();
+        for (int j = threadIdx.x; j < p.K; j += kThreads) {
+            const uint32_t i = sel.idx[j];
+            const uint32_t rank = wprefix[i >> 5] + __popc(bits[i >> 5] & ((1u << (i & 31)) - 1u));
+            out_i[rank] = int32_t(int64_t(i) * p.n_shards + s);
+            out_s[rank] = score_of(sel.key[j]);
+        }
+        return;
+    }
+    if (vec)
+        select_into_bitmap<4, false>(sh, LocalSrc4{scores}, n, uint32_t(p.K), bits);
+    else
+        select_into_bitmap<16, false>(sh, LocalSrc{scores}, n, uint32_t(p.K), bits);
+    // set bits in index order -> ascending positions
+    uint32_t cnt = 0;
+    for (int w = w0; w < w0 + per && w < words; ++w) cnt += __popc(bits[w]);
+    uint32_t total;
+    uint32_t pos = block_excl_scan_u32(cnt, sh.scan, total);
+    for (int w = w0; w < w0 + per && w < words; ++w) {
+        uint32_t m = bits[w];
+        while (m) {
+            const int bit = __builtin_ctz(m);
+            m &= m - 1;
+            const int64_t j = int64_t(w) * 32 + bit;
+            out_i[pos] = int32_t(j * p.n_shards + s);
+            out_s[pos] = canon(scores[j]);
+            ++pos;
+        }
+    }
+    for (int32_t i = int32_t(total) + threadIdx.x; i < p.K; i += kThreads) {
+        out_i[i] = -1;
+        out_s[i] = -INFINITY;
+    }
+}
+
+struct MergeSrc {
+    const int32_t* idx;
+    const float* score;
+    size_t list_stride;
+    int32_t k_in;
+    __device__ size_t at(int64_t i) const {
+        const uint32_t l = uint32_t(i) / uint32_t(k_in);
+        return size_t(l) * list_stride + (uint32_t(i) - l * uint32_t(k_in));
+    }
+    static constexpr int V = 1;
+    __device__ void keys(int64_t g, int64_t, uint64_t (&k)[V]) const {
+        const size_t a = at(g);
+        const int32_t id = idx[a];
+        k[0] = id >= 0 ? make_key(score[a], uint32_t(id)) : 0;
+    }
+};
+
+// Global top-K of one row from the shards' candidate lists.  Dynamic LDS:
+// a bitmap over the n_lists * k_in candidates, then the K chosen positions.
+__global__ void __launch_bounds__(kThreads) merge_topk_kernel(MergeParams p, int32_t bitmap_words) {
+    __shared__ SelectShared sh;
+    extern __shared__ uint32_t dyn[];
+    uint32_t* bits = dyn;
+    int32_t* chosen = reinterpret_cast<int32_t*>(dyn + bitmap_words);
+    const int64_t row = blockIdx.x;
+    const size_t list_stride = size_t(p.rows) * p.k_in;
+    const int32_t* idx = p.cand_idx + size_t(row) * p.k_in;
+    const float* sc = p.cand_score + size_t(row) * p.k_in;
+    const MergeSrc src{idx, sc, list_stride, p.k_in};
+    const int64_t n = int64_t(p.n_lists) * p.k_in;
+    for (int i = threadIdx.x; i < bitmap_words; i += kThreads) bits[i] = 0;
+    // valid candidates
+    uint32_t nv = 0;
+    for_each_key<16>(src, n, [&](int64_t, uint64_t) { ++nv; });
+    uint32_t n_valid;
+    block_excl_scan_u32(nv, sh.scan, n_valid);  // also orders the clearing above
+    if (n_valid <= uint32_t(p.K)) {
+        for_each_key<16>(src, n, [&](int64_t i, uint64_t) { atomicOr(&bits[i >> 5], 1u << (i & 31)); });
+        __syncthreads();
+    } else {
+        select_into_bitmap<16, false>(sh, src, n, uint32_t(p.K), bits);
+    }
+    // gather the chosen positions (bitmap order), then sort them ascending
+    const int per = (bitmap_words + kThreads - 1) / kThreads;
+    const int w0 = threadIdx.x * per;
+    uint32_t cnt = 0;
+    for (int w = w0; w < w0 + per && w < bitmap_words; ++w) cnt += __popc(bits[w]);
+    uint32_t total;
+    uint32_t pos = block_excl_scan_u32(cnt, sh.scan, total);
+    for (int w = w0; w < w0 + per && w < bitmap_words; ++w) {
+        uint32_t m = bits[w];
+        while (m) {
+            const int bit = __builtin_ctz(m);
+            m &= m - 1;
+            chosen[pos++] = idx[src.at(int64_t(w) * 32 + bit)];
+        }
+    }
+    uint32_t pw = 1;
+    while (pw < total) pw <<= 1;
+    for (uint32_t i = total + threadIdx.x; i < pw; i += kThreads) chosen[i] = INT32_MAX;
+    __syncthreads();
+    for (uint32_t size = 2; size <= pw; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t i = threadIdx.x; i < pw / 2; i += kThreads) {
+                const uint32_t lo = 2 * i - (i & (stride - 1));
+                const uint32_t hi = lo + stride;
+                const bool asc = (lo & size) == 0;
+                const int32_t a = chosen[lo], c = chosen[hi];
+                if ((a > c) == asc) {
+                    chosen[lo] = c;
+                    chosen[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    int32_t* out = p.out_idx + size_t(row) * p.K;
+    for (int32_t i = threadIdx.x; i < p.K; i += kThreads) out[i] = uint32_t(i) < total ? chosen[i] : -1;
+}
+
+// ---- rows read once into LDS --------------------------------------------
+//
+// A row of at most kStage elements is loaded into LDS in one sweep (16-byte
+// loads, all of a thread's loads in flight at once) and every later pass
+// reads LDS, so the scores cross HBM once.  128 KB of staging plus the
+// selection state fills one CU's LDS: one workgroup per CU.
+
+struct StagedMergeSrc {
+    static constexpr int V = 1;
+    const int32_t* idx;
+    const float* score;
+    __device__ void keys(int64_t g, int64_t, uint64_t (&k)[V]) const {
+        const int32_t id = idx[g];
+        k[0] = id >= 0 ? make_key(score[g], uint32_t(id)) : 0;
+    }
+};
+
+// n_lists * k_in <= kStage / 2 candidates, K <= kStageK.
+__global__ void __launch_bounds__(kThreads) merge_topk_staged_kernel(MergeParams p) {
+    constexpr int kN = kStage / 2;
+    __shared__ SelectShared sh;
+    __shared__ int32_t idx_s[kN];
+    __shared__ float sc_s[kN];
+    __shared__ uint32_t bits[kN / 32];
+    const int64_t row = blockIdx.x;
+    const size_t list_stride = size_t(p.rows) * p.k_in;
+    const int64_t n = int64_t(p.n_lists) * p.k_in;
+    {
+        // all of a thread's loads in flight before the first LDS store
+        constexpr int kPer = kN / kThreads;  // 32
+        int32_t vi[kPer];
+        float vs[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int64_t i = int64_t(j) * kThreads + threadIdx.x;
+            if (i < n) {
+                const uint32_t l = uint32_t(i) / uint32_t(p.k_in);
+                const size_t a = size_t(l) * list_stride + size_t(row) * p.k_in + (uint32_t(i) - l * uint32_t(p.k_in));
+                vi[j] = p.cand_idx[a];
+                vs[j] = p.cand_score[a];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int64_t i = int64_t(j) * kThreads + threadIdx.x;
+            if (i < n) {
+                idx_s[i] = vi[j];
+                sc_s[i] = vs[j];
+            }
+        }
+    }
+    const int32_t words = int32_t((n + 31) / 32);
+    for (int i = threadIdx.x; i < words; i += kThreads) bits[i] = 0;
+    __syncthreads();
+    const StagedMergeSrc src{idx_s, sc_s};
+    uint32_t nv = 0;
+    for_each_key<8>(src, n, [&](int64_t, uint64_t) { ++nv; });
+    uint32_t n_valid;
+    block_excl_scan_u32(nv, sh.scan, n_valid);
+    if (n_valid <= uint32_t(p.K)) {
+        for_each_key<8>(src, n, [&](int64_t i, uint64_t) { atomicOr(&bits[i >> 5], 1u << (i & 31)); });
+        __syncthreads();
+    } else {
+        select_into_bitmap<8, false>(sh, src, n, uint32_t(p.K), bits);
+    }
+    // the chosen positions, sorted ascending in the tied-group space
+    int32_t* chosen = reinterpret_cast<int32_t*>(sh.cand_key);
+    const int per = (words + kThreads - 1) / kThreads;
+    const int w0 = threadIdx.x * per;
+    uint32_t cnt = 0;
+    for (int w = w0; w < w0 + per && w < words; ++w) cnt += __popc(bits[w]);
+    uint32_t total;
+    uint32_t pos = block_excl_scan_u32(cnt, sh.scan, total);
+    for (int w = w0; w < w0 + per && w < words; ++w) {
+        uint32_t m = bits[w];
+        while (m) {
+            const int bit = __builtin_ctz(m);
+            m &= m - 1;
+            chosen[pos++] = idx_s[w * 32 + bit];
+        }
+    }
+    uint32_t pw = 1;
+    while (pw < total) pw <<= 1;
+    for (uint32_t i = total + threadIdx.x; i < pw; i += kThreads) chosen[i] = INT32_MAX;
+    __syncthreads();
+    for (uint32_t size = 2; size <= pw; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t i = threadIdx.x; i < pw / 2; i += kThreads) {
+                const uint32_t lo = 2 * i - (i & (stride - 1));
+                const uint32_t hi = lo + stride;
+                const bool asc = (lo & size) == 0;
+                const int32_t a = chosen[lo], c = chosen[hi];
+                if ((a > c) == asc) {
+                    chosen[lo] = c;
+                    chosen[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    int32_t* out = p.out_idx + size_t(row) * p.K;
+    for (int32_t i = threadIdx.x; i < p.K; i += kThreads) out[i] = uint32_t(i) < total ? chosen[i] : -1;
+}
+
+}  // namespace topk
+}  // namespace mla

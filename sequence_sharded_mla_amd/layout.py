@@ -142,3 +142,19 @@ def pack(x, device="cuda", extra_width=0):
                       context_lens=torch.from_numpy(x.context_lens.astype(np.int32)).to(device),
                       q=q, topk_idx=topk, n_shards=N, max_blocks=max_blocks,
                       tables_host=tables, desc=desc)
+
+
+def shard_scores(scores, n_shards):
+    """Global indexer scores [B][Tq][L] -> per-shard rows [N][B][Tq][ceil(L / N)].
+
+    Entry j of shard s is the score of global position j * N + s (the scores
+    a DCP rank computes for its own tokens); entries past the context are
+    -inf.
+    """
+    B, Tq, L = scores.shape
+    width = -(-L // n_shards)
+    out = np.full((n_shards, B, Tq, width), -np.inf, dtype=np.float32)
+    for s in range(n_shards):
+        part = scores[:, :, s::n_shards]
+        out[s, :, :, :part.shape[2]] = part
+    return out

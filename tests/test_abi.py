@@ -277,3 +277,38 @@ def test_fused_write_checks(lib):
     assert fw(pos=FAKE + 2) == _lib.MLA_ERR_ALIGN
     assert fw(ws=FAKE + 2) == _lib.MLA_ERR_ALIGN
     assert fw(n=0, src=None, req=None, pos=None, bt=None, pool=None) == 0
+
+
+def test_topk_checks(lib):
+    v = ctypes.c_void_p
+
+    def loc(sc=FAKE, stride=1000, ctx=FAKE, B=2, Tq=1, k=64, begin=0, count=8, N=8, ci=FAKE, cs=FAKE,
+            ws=None):
+        return lib.mla_topk_local(v(sc), stride, v(ctx), B, Tq, k, begin, count, N, v(ci), v(cs),
+                                  None if ws is None else v(ws), None)
+
+    assert loc(stride=0) == _lib.MLA_ERR_SHAPE
+    assert loc(stride=(1 << 19) + 1) == _lib.MLA_ERR_SHAPE
+    assert loc(k=0) == _lib.MLA_ERR_SHAPE
+    assert loc(Tq=0) == _lib.MLA_ERR_SHAPE
+    assert loc(B=-1) == _lib.MLA_ERR_SHAPE
+    assert loc(begin=1) == _lib.MLA_ERR_SHARD
+    assert loc(N=0, count=1) == _lib.MLA_ERR_SHARD
+    assert loc(sc=None) == _lib.MLA_ERR_NULL
+    assert loc(ctx=None) == _lib.MLA_ERR_NULL
+    assert loc(ci=None) == _lib.MLA_ERR_NULL
+    assert loc(cs=FAKE + 2) == _lib.MLA_ERR_ALIGN
+    assert loc(ws=FAKE + 1) == _lib.MLA_ERR_ALIGN
+    assert loc(B=0, sc=None) == 0
+
+    def mer(ci=FAKE, cs=FAKE, n=8, rows=10, ck=2048, k=2048, out=FAKE):
+        return lib.mla_topk_merge(v(ci), v(cs), n, rows, ck, k, v(out), None)
+
+    assert mer(n=0) == _lib.MLA_ERR_SHAPE
+    assert mer(rows=-1) == _lib.MLA_ERR_SHAPE
+    assert mer(k=8193) == _lib.MLA_ERR_SHAPE
+    assert mer(n=200) == _lib.MLA_ERR_SHAPE
+    assert mer(ck=0) == _lib.MLA_ERR_SHAPE
+    assert mer(out=None) == _lib.MLA_ERR_NULL
+    assert mer(ci=FAKE + 2) == _lib.MLA_ERR_ALIGN
+    assert mer(rows=0) == 0

@@ -263,3 +263,26 @@ def new_token_rows(n, seed, dtype="bf16", spread=0):
             x *= np.exp2(rng.integers(-spread, spread + 1, (m, 1))).astype(np.float32)
         out[r0:r0 + m] = x if dtype == "f32" else _bf16_bits(x)
     return out
+
+
+# Indexer scores for top-K selection: the scoring model needs trained
+# weights, so scores are seeded N(0, 1) draws over each request's whole
+# context (global positions), optionally rounded to bf16 so that equal
+# scores are common.  The selection workload has the shape of
+# sparse_fp8_topk2048: 128 requests x 2 query tokens, context 262144,
+# top-2048, 8 shards.
+SELECT_SPECS = {
+    "topk_select_262k": dict(batch=128, q_len=2, context=262144, topk=2048, n_shards=8, seed=707),
+}
+
+
+def indexer_scores(batch, q_len, context, seed, ties=False):
+    """Seeded scores [batch][q_len][context] float32."""
+    out = np.empty((batch, q_len, context), np.float32)
+    for b in range(batch):
+        rng = np.random.default_rng([seed, 9, b])
+        x = rng.standard_normal((q_len, context), dtype=np.float32)
+        if ties:
+            x = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+        out[b] = x
+    return out
