@@ -22,8 +22,7 @@
 // the prefix found so far (LDS atomics), then a suffix scan picks the digit
 // holding the K-th key.  As soon as the tied group is small enough
 // (<= kCand), one more pass over the row sets a bit for every element above
-// the group and copies the group into LDS, where a bitonic sort by key
-// settles it.  The set bits, read in index order, give the output; a row
+// the group and copies the group into LDS, where 8-bit digits settle it.  The set bits, read in index order, give the output; a row
 // usually needs two passes over its scores (one from HBM, one from cache).
 #pragma once
 
@@ -86,15 +85,22 @@ __device__ __forceinline__ int digit_shift(int pass) {
 }
 __device__ __forceinline__ int digit_width(int pass) { return (pass % 3 == 2) ? 8 : 12; }
 
-// The selected elements of a row (key and index, in no particular order).
+// Elements of a row kept in LDS: the score bits of the key (its high 32
+// bits; the low 32 are the complement of the index) and the index.
+constexpr int kBuf = 4096;
 struct SelList {
-    uint64_t key[kSel];
-    uint32_t idx[kSel];
+    uint32_t sb[kBuf];
+    uint32_t idx[kBuf];
     uint32_t n;
 };
 
+__device__ __forceinline__ uint64_t key_of(uint32_t sb, uint32_t idx) {
+    return (uint64_t(sb) << 32) | uint64_t(~idx);
+}
+
 struct SelectShared {
-    // the histogram serves the digit passes, the tied group the last pass
+    // the histogram serves the digit passes over the row, the tied group
+    // the last pass and its settling in LDS
     union {
         uint32_t hist[kBins];
         struct {
@@ -102,6 +108,7 @@ struct SelectShared {
             uint32_t cand_idx[kCand];
         };
     };
+    uint32_t hist8[256];     // 8-bit digits of the tied group in LDS
     uint64_t prefix;         // fixed top bits of the K-th key
     uint64_t mask;           // which bits are fixed
     uint32_t need;           // elements still to take from the tied group
@@ -133,21 +140,9 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t x, uint32_t* wa
     return before + inc - x;
 }
 
-// Slot of this lane among the lanes of its wave that append (pred), taken
-// from `counter` with one atomic per wave.  Every active lane must call it.
-__device__ __forceinline__ uint32_t wave_append(uint32_t* counter, bool pred) {
-    const uint64_t m = __ballot(pred);
-    if (!m) return 0;
-    const int leader = __builtin_ctzll(m);
-    uint32_t base = 0;
-    if ((threadIdx.x & 63) == leader) base = atomicAdd(counter, uint32_t(__popcll(m)));
-    base = __shfl(base, leader);
-    return base + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-}
-
 // Finds the digit holding the need-th largest key among the histogram's
 // bins (nbins <= kBins), updates prefix/mask/need/tied.  All threads call.
-__device__ __forceinline__ void pick_digit(SelectShared& sh, int nbins, int shift) {
+__device__ __forceinline__ void pick_digit(SelectShared& sh, const uint32_t* hist, int nbins, int shift) {
     // each thread sums a contiguous run of bins, counted from the top bin down
     constexpr int kPer = kBins / kThreads;  // 8
     const int per = nbins / kThreads > 0 ? nbins / kThreads : 1;
@@ -155,7 +150,7 @@ __device__ __forceinline__ void pick_digit(SelectShared& sh, int nbins, int shif
     uint32_t mine = 0;
     const int t = threadIdx.x;
     if (t < active) {
-        for (int j = 0; j < per && j < kPer; ++j) mine += sh.hist[nbins - 1 - (t * per + j)];
+        for (int j = 0; j < per && j < kPer; ++j) mine += hist[nbins - 1 - (t * per + j)];
     }
     const uint32_t need = sh.need;  // read before the scan's barriers: one thread rewrites it
     uint32_t total;
@@ -164,7 +159,7 @@ __device__ __forceinline__ void pick_digit(SelectShared& sh, int nbins, int shif
         uint32_t above = before;
         for (int j = 0; j < per; ++j) {
             const int bin = nbins - 1 - (t * per + j);
-            const uint32_t c = sh.hist[bin];
+            const uint32_t c = hist[bin];
             if (need <= above + c) {
                 sh.prefix |= uint64_t(bin) << shift;
                 sh.mask |= uint64_t(nbins - 1) << shift;
@@ -176,37 +171,6 @@ __device__ __forceinline__ void pick_digit(SelectShared& sh, int nbins, int shif
         }
     }
     __syncthreads();
-}
-
-// Bitonic sort of sh.cand_key / cand_idx [0, n) descending by key, padding
-// up to the next power of two with key 0 (below every real key, whose score
-// bits are non-zero).
-__device__ __forceinline__ void sort_candidates_desc(SelectShared& sh, uint32_t n) {
-    uint32_t p = 1;
-    while (p < n) p <<= 1;
-    for (uint32_t i = n + threadIdx.x; i < p; i += kThreads) {
-        sh.cand_key[i] = 0;
-        sh.cand_idx[i] = 0;
-    }
-    __syncthreads();
-    for (uint32_t size = 2; size <= p; size <<= 1) {
-        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-            for (uint32_t i = threadIdx.x; i < p / 2; i += kThreads) {
-                const uint32_t lo = 2 * i - (i & (stride - 1));
-                const uint32_t hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const uint64_t a = sh.cand_key[lo], b = sh.cand_key[hi];
-                if ((a < b) == desc) {
-                    sh.cand_key[lo] = b;
-                    sh.cand_key[hi] = a;
-                    const uint32_t ia = sh.cand_idx[lo];
-                    sh.cand_idx[lo] = sh.cand_idx[hi];
-                    sh.cand_idx[hi] = ia;
-                }
-            }
-            __syncthreads();
-        }
-    }
 }
 
 // Calls f(i, key) for every element i < n whose key is not 0 (0 marks an
@@ -260,15 +224,21 @@ __device__ void select_into_bitmap(SelectShared& sh, const Src& src, int64_t n, 
             if ((k & mask) == prefix) atomicAdd(&sh.hist[uint32_t(k >> shift) & uint32_t(nbins - 1)], 1u);
         });
         __syncthreads();
-        pick_digit(sh, nbins, shift);
+        pick_digit(sh, sh.hist, nbins, shift);
     }
     // one pass: elements above the tied group are selected; the group goes
     // to LDS unless all of it is taken
     const uint64_t prefix = sh.prefix, mask = sh.mask;
     const bool take_all = sh.tied == sh.need;
+    // Appends go through one wave-wide scan and one LDS atomic per list per
+    // batch: each lane counts its selected and tied elements, a wave scan
+    // turns the counts into slots.  The loop runs the same number of
+    // batches in every lane, so the wave is whole for the scan.
     constexpr int V = Src::V;
     const int64_t groups = (n + V - 1) / V;
-    for (int64_t g0 = threadIdx.x; g0 < groups; g0 += int64_t(kThreads) * U) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t base = 0; base < groups; base += int64_t(kThreads) * U) {
+        const int64_t g0 = base + threadIdx.x;
         uint64_t k[U][V];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -279,6 +249,7 @@ __device__ void select_into_bitmap(SelectShared& sh, const Src& src, int64_t n, 
                 for (int v = 0; v < V; ++v) k[u][v] = 0;
             }
         }
+        uint32_t counts = 0;  // selected in the low 16 bits, tied in the high 16
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -289,43 +260,102 @@ __device__ void select_into_bitmap(SelectShared& sh, const Src& src, int64_t n, 
                 const bool is_sel = kk && (top > prefix || (top == prefix && take_all));
                 const bool tie = kk && top == prefix && !take_all;
                 if (is_sel) atomicOr(&bits[i >> 5], 1u << (i & 31));
-                if (COLLECT) {
-                    const uint32_t at = wave_append(&sel->n, is_sel);
-                    if (is_sel) {
-                        sel->key[at] = kk;
-                        sel->idx[at] = uint32_t(i);
+                counts += (COLLECT && is_sel ? 1u : 0u) + (tie ? 0x10000u : 0u);
+            }
+        }
+        uint32_t incl = counts;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        const uint32_t tot = __shfl(incl, 63);
+        if (tot == 0) continue;
+        uint32_t bases = 0;
+        if (lane == 0) {
+            const uint32_t bs = (COLLECT && (tot & 0xffffu)) ? atomicAdd(&sel->n, tot & 0xffffu) : 0u;
+            const uint32_t bt = (tot >> 16) ? atomicAdd(&sh.n_cand, tot >> 16) : 0u;
+            bases = bs | (bt << 16);  // both below 2^16
+        }
+        bases = __shfl(bases, 0);
+        const uint32_t excl = incl - counts;
+        uint32_t at_sel = (bases & 0xffffu) + (excl & 0xffffu);
+        uint32_t at_tie = (bases >> 16) + (excl >> 16);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int64_t i = (g0 + int64_t(u) * kThreads) * V + v;
+                const uint64_t kk = k[u][v];
+                const uint64_t top = kk & mask;
+                const bool is_sel = kk && (top > prefix || (top == prefix && take_all));
+                const bool tie = kk && top == prefix && !take_all;
+                // the bounds hold by construction (at most K selected, the
+                // tied group fits); the checks keep a broken invariant in LDS
+                if (COLLECT && is_sel) {
+                    if (at_sel < uint32_t(kBuf)) {
+                        sel->sb[at_sel] = uint32_t(kk >> 32);
+                        sel->idx[at_sel] = uint32_t(i);
                     }
+                    ++at_sel;
                 }
-                const uint32_t slot = wave_append(&sh.n_cand, tie);
                 if (tie) {
-                    sh.cand_key[slot] = kk;
-                    sh.cand_idx[slot] = uint32_t(i);
+                    if (at_tie < uint32_t(kCand)) {
+                        sh.cand_key[at_tie] = kk;
+                        sh.cand_idx[at_tie] = uint32_t(i);
+                    }
+                    ++at_tie;
                 }
             }
         }
     }
     __syncthreads();
     if (!take_all) {
-        const uint32_t nc = sh.n_cand;
+        // the tied group is in LDS: settle it with 8-bit digits of the
+        // bits not fixed yet, down to a group taken whole (keys are distinct)
+        const uint32_t nc = sh.n_cand < uint32_t(kCand) ? sh.n_cand : uint32_t(kCand);
+        int shift = 64;
+        while (shift > 0 && ((sh.mask >> (shift - 1)) & 1u)) --shift;  // highest free bit + 1
+        shift = shift > 8 ? shift - 8 : 0;
+        while (sh.tied != sh.need) {
+            for (int i = threadIdx.x; i < 256; i += kThreads) sh.hist8[i] = 0;
+            __syncthreads();
+            const uint64_t pre = sh.prefix, msk = sh.mask;
+            for (uint32_t j = threadIdx.x; j < nc; j += kThreads) {
+                const uint64_t kk = sh.cand_key[j];
+                if ((kk & msk) == pre) atomicAdd(&sh.hist8[uint32_t(kk >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            pick_digit(sh, sh.hist8, 256, shift);
+            shift = shift > 8 ? shift - 8 : 0;
+        }
+        const uint64_t pre = sh.prefix, msk = sh.mask;
         const uint32_t ns = COLLECT ? sel->n : 0;
-        sort_candidates_desc(sh, nc);
-        for (uint32_t j = threadIdx.x; j < sh.need; j += kThreads) {
-            const uint32_t i = sh.cand_idx[j];
-            atomicOr(&bits[i >> 5], 1u << (i & 31));
-            if (COLLECT) {
-                sel->key[ns + j] = sh.cand_key[j];
-                sel->idx[ns + j] = i;
+        uint32_t mine = 0;
+        for (uint32_t j = threadIdx.x; j < nc; j += kThreads) mine += (sh.cand_key[j] & msk) >= pre ? 1u : 0u;
+        uint32_t total;
+        uint32_t at = ns + block_excl_scan_u32(mine, sh.scan, total);
+        for (uint32_t j = threadIdx.x; j < nc; j += kThreads) {
+            const uint64_t kk = sh.cand_key[j];
+            if ((kk & msk) >= pre) {
+                const uint32_t i = sh.cand_idx[j];
+                atomicOr(&bits[i >> 5], 1u << (i & 31));
+                if (COLLECT && at < uint32_t(kBuf)) {
+                    sel->sb[at] = uint32_t(kk >> 32);
+                    sel->idx[at] = i;
+                }
+                ++at;
             }
         }
     }
     __syncthreads();
 }
 
-// A score row read one float per element.
 struct LocalSrc {
     static constexpr int V = 1;
     const float* row;
     __device__ void keys(int64_t g, int64_t, uint64_t (&k)[V]) const { k[0] = make_key(row[g], uint32_t(g)); }
+    __device__ void load(int64_t g, float (&x)[V]) const { x[0] = row[g]; }
 };
 
 // A score row read 16 bytes (four elements) per load; the row is 16-byte
@@ -341,22 +371,168 @@ struct LocalSrc4 {
             k[v] = i < n ? make_key(x[v], uint32_t(i)) : 0;
         }
     }
+    __device__ void load(int64_t g, float (&x)[V]) const {
+        const f32x4_t y = reinterpret_cast<const f32x4_t*>(row)[g];
+        x[0] = y[0];
+        x[1] = y[1];
+        x[2] = y[2];
+        x[3] = y[3];
+    }
 };
 
 // A candidate score as returned: the stored score, with -0 written as +0
 // (the two are one value for the selection).
 __device__ __forceinline__ float canon(float x) { return x == 0.f ? 0.f : x; }
 
-// The score a key was made from (canonical: -0 comes back as +0).
-__device__ __forceinline__ float score_of(uint64_t key) {
-    const uint32_t b = uint32_t(key >> 32);
+// The score given its order-preserving bits (canonical: -0 comes back as +0).
+__device__ __forceinline__ float score_of(uint32_t b) {
     return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
+
+// Settles a tied group held in LDS: `count` entries of `buf`, those whose
+// key matches sh.prefix under sh.mask are tied, sh.need of them are taken.
+// Adds 8-bit digits below the fixed bits until the group is taken whole.
+__device__ void settle_in_lds(SelectShared& sh, const SelList& buf, uint32_t count) {
+    int shift = 64;
+    while (shift > 0 && ((sh.mask >> (shift - 1)) & 1u)) --shift;
+    shift = shift > 8 ? shift - 8 : 0;
+    while (sh.tied != sh.need) {
+        for (int i = threadIdx.x; i < 256; i += kThreads) sh.hist8[i] = 0;
+        __syncthreads();
+        const uint64_t pre = sh.prefix, msk = sh.mask;
+        for (uint32_t j = threadIdx.x; j < count; j += kThreads) {
+            const uint64_t kk = key_of(buf.sb[j], buf.idx[j]);
+            if ((kk & msk) == pre) atomicAdd(&sh.hist8[uint32_t(kk >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        pick_digit(sh, sh.hist8, 256, shift);
+        shift = shift > 8 ? shift - 8 : 0;
+    }
+}
+
+// One read of the row: a 512-element sample places a first digit D a little
+// below the K-th key's; the pass over the row counts the 12-bit digits of,
+// and keeps in LDS, every element whose digit is at least D.  When the K-th key's digit turns
+// out to be at least D (and the kept set fit), the whole selection is among
+// the kept elements and settles in LDS; `buf` then holds them and the ones
+// chosen satisfy (key & sh.mask) >= sh.prefix.  Returns false otherwise (no
+// bit set; the caller runs the general selection).
+template <int U, typename Src>
+__device__ bool select_one_pass(SelectShared& sh, SelList& buf, const Src& src, const float* row,
+                                int64_t n, uint32_t K, uint32_t* bits) {
+    for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist[i] = 0;
+    if (threadIdx.x == 0) {
+        sh.prefix = 0;
+        sh.mask = 0;
+        sh.need = K;
+        sh.tied = uint32_t(n);
+        buf.n = 0;
+    }
+    __syncthreads();
+    // raw scores stay in registers (4 bytes each) until they are used
+    uint32_t d_min = 0;
+    constexpr int V = Src::V;
+    const int64_t groups = (n + V - 1) / V;
+    const int lane = threadIdx.x & 63;
+    for (int64_t base = 0; base < groups; base += int64_t(kThreads) * U) {
+        const int64_t g0 = base + threadIdx.x;
+        float x[U][V];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = g0 + int64_t(u) * kThreads;
+            if (g < groups) src.load(g, x[u]);
+        }
+        if (base == 0 && n > kBuf) {
+            // the sample's load goes out behind the first batch's, so the
+            // wait for it costs no extra round trip
+            const int64_t i = int64_t(threadIdx.x) * (n / kThreads);
+            atomicAdd(&sh.hist[uint32_t(make_key(row[i], uint32_t(i)) >> 52)], 1u);
+            __syncthreads();
+            // the kept share of the sample plus a few: the digit's bins are
+            // coarse (about 1.5% of a normal row near the top 6%), so the
+            // kept set already has slack; a row whose estimate misses takes
+            // the general path
+            uint32_t need_s = uint32_t((uint64_t(K) * kThreads + n - 1) / uint64_t(n)) + 8;
+            if (need_s > uint32_t(kThreads)) need_s = kThreads;
+            if (threadIdx.x == 0) sh.need = need_s;
+            __syncthreads();
+            pick_digit(sh, sh.hist, kBins, 52);
+            d_min = uint32_t(sh.prefix >> 52);
+            __syncthreads();  // every thread has read the sample's digit
+            for (int j = threadIdx.x; j < kBins; j += kThreads) sh.hist[j] = 0;
+            if (threadIdx.x == 0) {
+                sh.prefix = 0;
+                sh.mask = 0;
+                sh.need = K;
+                sh.tied = uint32_t(n);
+            }
+            __syncthreads();
+        }
+        // digit of element (u, v), or 0 when it is past the row
+        auto digit = [&](int u, int v) -> uint32_t {
+            const int64_t i = (g0 + int64_t(u) * kThreads) * V + v;
+            return i < n ? score_bits(x[u][v]) >> 20 : 0u;
+        };
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const uint32_t d = digit(u, v);
+                // only digits >= D are counted: the K-th key's digit is found
+                // among them or the row takes the general path (d_min >= 1
+                // whenever past-the-row elements could pass)
+                if (d >= d_min && (d_min > 0 || (g0 + int64_t(u) * kThreads) * V + v < n)) {
+                    atomicAdd(&sh.hist[d], 1u);
+                    ++cnt;
+                }
+            }
+        uint32_t incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        const uint32_t tot = __shfl(incl, 63);
+        if (tot == 0) continue;
+        uint32_t at = 0;
+        if (lane == 0) at = atomicAdd(&buf.n, tot);
+        at = __shfl(at, 0) + incl - cnt;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int64_t i = (g0 + int64_t(u) * kThreads) * V + v;
+                const uint32_t d = digit(u, v);
+                if (!(d >= d_min && (d_min > 0 || i < n))) continue;
+                if (at < uint32_t(kBuf)) {
+                    buf.sb[at] = score_bits(x[u][v]);
+                    buf.idx[at] = uint32_t(i);
+                }
+                ++at;
+            }
+    }
+    __syncthreads();
+    pick_digit(sh, sh.hist, kBins, 52);
+    const uint32_t kept = buf.n;
+    const bool fits = kept <= uint32_t(kBuf) && uint32_t(sh.prefix >> 52) >= d_min;
+    __syncthreads();  // the caller may reset the state next
+    if (!fits) return false;
+    settle_in_lds(sh, buf, kept);
+    const uint64_t pre = sh.prefix, msk = sh.mask;
+    for (uint32_t j = threadIdx.x; j < kept; j += kThreads) {
+        const uint32_t i = buf.idx[j];
+        if ((key_of(buf.sb[j], i) & msk) >= pre) atomicOr(&bits[i >> 5], 1u << (i & 31));
+    }
+    __syncthreads();
+    return true;
 }
 
 // Local top-K of one (shard, request, query token) row.  Dynamic LDS: the
 // bitmap (one bit per local position of the longest row of the launch) and
 // the running count of set bits before each bitmap word.
-__global__ void __launch_bounds__(kThreads) local_topk_kernel(LocalParams p, int32_t bitmap_words) {
+// Two workgroups per CU (LDS allows it): at most 128 VGPRs.
+__global__ void __launch_bounds__(kThreads, 4) local_topk_kernel(LocalParams p, int32_t bitmap_words) {
     __shared__ SelectShared sh;
     __shared__ SelList sel;
     extern __shared__ uint32_t dyn[];
@@ -391,10 +567,21 @@ __global__ void __launch_bounds__(kThreads) local_topk_kernel(LocalParams p, int
     const int w0 = threadIdx.x * per;
     const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && (p.stride & 3) == 0;
     if (p.K <= kSel) {
-        if (vec)
-            select_into_bitmap<4, true>(sh, LocalSrc4{scores}, n, uint32_t(p.K), bits, &sel);
-        else
-            select_into_bitmap<16, true>(sh, LocalSrc{scores}, n, uint32_t(p.K), bits, &sel);
+        // one read of the row when the sample's estimate holds; else the
+        // digit passes, listing the kept elements as they are marked
+        const bool one = vec ? select_one_pass<8>(sh, sel, LocalSrc4{scores}, scores, n, uint32_t(p.K), bits)
+                             : select_one_pass<16>(sh, sel, LocalSrc{scores}, scores, n, uint32_t(p.K), bits);
+        uint32_t listed = uint32_t(p.K);
+        uint64_t pre = 0, msk = 0;
+        if (one) {
+            listed = sel.n;
+            pre = sh.prefix;
+            msk = sh.mask;
+        } else if (vec) {
+            select_into_bitmap<2, true>(sh, LocalSrc4{scores}, n, uint32_t(p.K), bits, &sel);
+        } else {
+            select_into_bitmap<8, true>(sh, LocalSrc{scores}, n, uint32_t(p.K), bits, &sel);
+        }
         // output slot of a kept element = kept elements before it
         uint32_t cnt = 0;
         for (int w = w0; w < w0 + per && w < words; ++w) cnt += __popc(bits[w]);
@@ -405,18 +592,21 @@ __global__ void __launch_bounds__(kThreads) local_topk_kernel(LocalParams p, int
             run += __popc(bits[w]);
         }
         __syncthreads();
-        for (int j = threadIdx.x; j < p.K; j += kThreads) {
+        for (uint32_t j = threadIdx.x; j < listed && j < uint32_t(kBuf); j += kThreads) {
             const uint32_t i = sel.idx[j];
+            if (one && (key_of(sel.sb[j], i) & msk) < pre) continue;  // kept in LDS, not chosen
             const uint32_t rank = wprefix[i >> 5] + __popc(bits[i >> 5] & ((1u << (i & 31)) - 1u));
-            out_i[rank] = int32_t(int64_t(i) * p.n_shards + s);
-            out_s[rank] = score_of(sel.key[j]);
+            if (rank < uint32_t(p.K)) {  // exactly K are chosen; the check guards the output row
+                out_i[rank] = int32_t(int64_t(i) * p.n_shards + s);
+                out_s[rank] = score_of(sel.sb[j]);
+            }
         }
         return;
     }
     if (vec)
-        select_into_bitmap<4, false>(sh, LocalSrc4{scores}, n, uint32_t(p.K), bits);
+        select_into_bitmap<2, false>(sh, LocalSrc4{scores}, n, uint32_t(p.K), bits);
     else
-        select_into_bitmap<16, false>(sh, LocalSrc{scores}, n, uint32_t(p.K), bits);
+        select_into_bitmap<8, false>(sh, LocalSrc{scores}, n, uint32_t(p.K), bits);
     // set bits in index order -> ascending positions
     uint32_t cnt = 0;
     for (int w = w0; w < w0 + per && w < words; ++w) cnt += __popc(bits[w]);
@@ -458,7 +648,7 @@ struct MergeSrc {
 
 // Global top-K of one row from the shards' candidate lists.  Dynamic LDS:
 // a bitmap over the n_lists * k_in candidates, then the K chosen positions.
-__global__ void __launch_bounds__(kThreads) merge_topk_kernel(MergeParams p, int32_t bitmap_words) {
+__global__ void __launch_bounds__(kThreads, 4) merge_topk_kernel(MergeParams p, int32_t bitmap_words) {
     __shared__ SelectShared sh;
     extern __shared__ uint32_t dyn[];
     uint32_t* bits = dyn;
