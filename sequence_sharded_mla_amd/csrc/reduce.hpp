@@ -71,14 +71,43 @@ template <typename T>
 __device__ __forceinline__ void merge_wave(int n, const T* o, size_t part_stride, const float* lse,
                                            size_t lse_stride, void* out, int out_dtype,
                                            size_t out_off, float* lse_out, int lane) {
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < n; s0 += 64)
-        M = fmaxf(M, s0 + lane < n ? lse[size_t(s0 + lane) * lse_stride] : -INFINITY);
-    M = wave_max(M);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float W = 0.f;
+    float M = -INFINITY;
     const T* base = o + lane * 8;
     constexpr int kBatch = 8;  // parts whose loads are in flight together
+    if (n <= 64) {
+        // one LSE per lane, and the first batch of parts requested together
+        // with it: the data does not wait for the weights
+        const float ls = lane < n ? lse[size_t(lane) * lse_stride] : -INFINITY;
+        float v[kBatch][8];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (k < n) load8<T>(base + size_t(k) * part_stride, v[k]);
+        M = wave_max(ls);
+        const float w = (ls == -INFINITY) ? 0.f : expf(ls - M);  // M = -inf: every w is 0
+        W = w;
+        for (int k0 = 0; k0 < n; k0 += kBatch) {
+            if (k0 > 0) {
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    if (k0 + k < n) load8<T>(base + size_t(k0 + k) * part_stride, v[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                if (k0 + k >= n) break;
+                const float ws = __shfl(w, k0 + k);
+                if (ws != 0.f) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[k][e], acc[e]);
+                }
+            }
+        }
+        n = 0;  // done: skip the general loop below
+    }
+    for (int s0 = 0; s0 < n; s0 += 64)
+        M = fmaxf(M, s0 + lane < n ? lse[size_t(s0 + lane) * lse_stride] : -INFINITY);
+    if (n > 0) M = wave_max(M);
     for (int s0 = 0; s0 < n; s0 += 64) {
         const float ls = s0 + lane < n ? lse[size_t(s0 + lane) * lse_stride] : -INFINITY;
         const float w = (ls == -INFINITY) ? 0.f : expf(ls - M);  // M = -inf: every w is 0
