@@ -114,6 +114,67 @@ def mla_decode(q, rows, context_lens, q_len, n_shards, scale,
     return out
 
 
+def varlen_tokens(query_start_loc):
+    """(request, index in it, the request's count) for every query token of
+    a call whose request b holds tokens query_start_loc[b] .. [b + 1] - 1."""
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    if qsl.ndim != 1 or qsl.size < 1 or qsl[0] != 0 or np.any(np.diff(qsl) < 0):
+        raise ValueError("query_start_loc must start at 0 and not decrease")
+    out = []
+    for b in range(qsl.size - 1):
+        c = int(qsl[b + 1] - qsl[b])
+        out.extend((b, t, c) for t in range(c))
+    return out
+
+
+def mla_decode_varlen(q, rows, context_lens, query_start_loc, n_shards, scale,
+                      topk_idx=None, tokens=None):
+    """The decode step when requests carry different numbers of query tokens
+    (multi-token prediction drafts; "GLM-5.2 vLLM Decode Context
+    Parallelism", section "See why vLLM 0.26.0 fails": the DCP backend must
+    accept the varlen-decode layout).
+
+    Reading taken: a request with c query tokens is the fixed form with
+    Tq = c, so its token t sits at position L_b - c + t and sees positions
+    0 .. L_b - c + t; only the count varies from request to request.
+
+    q            float64 [n_q, H, 576], tokens of request b at rows
+                 query_start_loc[b] .. query_start_loc[b + 1] - 1
+    topk_idx     int [n_q, K] global indices (-1 = none) or None (dense)
+    tokens       subset of query-token rows to evaluate (default: all)
+
+    Returns o_shards [N, T, H, 512], lse_shards [N, T, H], o [T, H, 512],
+    lse [T, H] over the evaluated tokens T in the given order.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_q, H, D = q.shape
+    assert D == DK
+    where = varlen_tokens(query_start_loc)
+    if len(where) != n_q:
+        raise ValueError("query_start_loc does not cover the query rows")
+    tokens = list(range(n_q)) if tokens is None else list(tokens)
+    T = len(tokens)
+    o_sh = np.zeros((n_shards, T, H, DV))
+    lse_sh = np.zeros((n_shards, T, H))
+    o = np.zeros((T, H, DV))
+    lse = np.zeros((T, H))
+    for ti, i in enumerate(tokens):
+        b, t, c = where[i]
+        last = int(context_lens[b]) - c + t
+        if topk_idx is None:
+            P = np.arange(max(last + 1, 0), dtype=np.int64)
+        else:
+            P = np.asarray(topk_idx[i], dtype=np.int64)
+            P = P[P >= 0]
+            if P.size and P.max() > last:
+                raise ValueError("top-K index outside the causal prefix")
+        for s in range(n_shards):
+            Ps = sharding.shard_positions(P, s, n_shards)
+            o_sh[s, ti], lse_sh[s, ti] = _attend_positions(q[i], rows, b, Ps, scale)
+        o[ti], lse[ti] = _attend_positions(q[i], rows, b, P, scale)
+    return {"o_shards": o_sh, "lse_shards": lse_sh, "o": o, "lse": lse}
+
+
 def query_to_f64(q, q_dtype):
     """Stored query (float32, or bf16 bits as uint16) -> float64."""
     from . import codecs

@@ -161,3 +161,69 @@ def test_brute_force_scalar_loops():
                         o_m[d] += w * o[d]
                 assert abs(r["lse"][b, t, h] - (m + math.log(wsum))) < 1e-12
                 assert np.allclose(r["o"][b, t, h], o_m, atol=1e-12)
+
+
+def _masked_softmax_attention(q, keys, visible, scale):
+    """Textbook attention of q [H, 576] over all keys with positions >=
+    visible masked to -inf (scipy's softmax and logsumexp)."""
+    from scipy.special import logsumexp, softmax
+    s = (q @ keys.T) * scale
+    s[:, visible:] = -np.inf
+    if visible <= 0:
+        return np.zeros((q.shape[0], 512)), np.full(q.shape[0], -np.inf)
+    return softmax(s, axis=1) @ keys[:, :512], logsumexp(s, axis=1)
+
+
+def test_varlen_matches_masked_softmax_per_token():
+    # requests with 2, 0, 3, 1 query tokens; the causal limit moves with the
+    # request's own count
+    rng = np.random.default_rng(21)
+    lens = [9, 4, 30, 2]
+    counts = [2, 0, 3, 1]
+    qsl = np.concatenate([[0], np.cumsum(counts)])
+    H, N = 2, 3
+    store = [rng.standard_normal((L, 576)) for L in lens]
+    q = rng.standard_normal((int(qsl[-1]), H, 576))
+
+    def rows(b, pos):
+        r = store[b][np.asarray(pos, dtype=np.int64)]
+        return r[:, :512], r[:, 512:]
+    r = decode.mla_decode_varlen(q, rows, np.array(lens), qsl, N, SCALE)
+    i = 0
+    for b, c in enumerate(counts):
+        for t in range(c):
+            o, l = _masked_softmax_attention(q[i], store[b], lens[b] - c + t + 1, SCALE)
+            assert np.allclose(r["o"][i], o, atol=1e-12) and np.allclose(r["lse"][i], l, atol=1e-12)
+            om, lm = attention.merge(r["o_shards"][:, i], r["lse_shards"][:, i])
+            assert np.allclose(om, o, atol=1e-12) and np.allclose(lm, l, atol=1e-12)
+            i += 1
+    # the newest token of each request sees its whole context, itself included
+    assert np.allclose(r["o"][1], _sdpa(q[1], store[0], SCALE), atol=1e-12)
+
+
+def test_varlen_sparse_and_token_subset():
+    rng = np.random.default_rng(22)
+    lens, counts, N = [50, 80], [3, 1], 4
+    qsl = np.array([0, 3, 4])
+    store = [rng.standard_normal((L, 576)) for L in lens]
+    q = rng.standard_normal((4, 2, 576))
+    idx = np.full((4, 6), -1, dtype=np.int32)
+    idx[0, :3] = [0, 47, 10]        # token 0 of request 0 sees up to 47
+    idx[2, :2] = [49, 3]
+    idx[3, :4] = [79, 0, 1, 2]
+
+    def rows(b, pos):
+        r = store[b][np.asarray(pos, dtype=np.int64)]
+        return r[:, :512], r[:, 512:]
+    r = decode.mla_decode_varlen(q, rows, np.array(lens), qsl, N, SCALE, topk_idx=idx, tokens=[3, 0, 1])
+    for ti, (i, b) in enumerate([(3, 1), (0, 0), (1, 0)]):
+        sel = idx[i][idx[i] >= 0]
+        o, l = attention.attend(q[i], store[b][sel], store[b][sel][:, :512], SCALE)
+        assert np.allclose(r["o"][ti], o, atol=1e-12) and np.allclose(r["lse"][ti], l, atol=1e-12)
+    assert np.all(np.isneginf(r["lse"][2]))          # token 1 has no index
+    bad = idx.copy()
+    bad[0, 0] = 48                                   # beyond L - 3 + 0
+    with pytest.raises(ValueError):
+        decode.mla_decode_varlen(q, rows, np.array(lens), qsl, N, SCALE, topk_idx=bad)
+    with pytest.raises(ValueError):
+        decode.mla_decode_varlen(q, rows, np.array(lens), np.array([0, 3, 2]), N, SCALE)
