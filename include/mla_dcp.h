@@ -90,6 +90,7 @@ extern "C" {
 #define MLA_DEVERR_INDEX 2u       /* top-K index beyond the causal prefix      */
 #define MLA_DEVERR_SLOT 4u        /* cache-write slot at or past the pool end  */
 #define MLA_DEVERR_SCORES 8u      /* score row shorter than the visible prefix */
+#define MLA_DEVERR_QUERY 16u      /* varlen query offsets not a partition      */
 
 /* Shape of one decode step.  Fixed by this build: kv_lora_rank = 512,
  * rope_dim = 64, block_size = 64; num_heads in {16, 32, 64, 128} (the query
@@ -160,6 +161,34 @@ int32_t mla_decode_partial_shards(const mla_decode_desc* desc, const void* q,
                                   int32_t shard_begin, int32_t shard_count, int32_t n_shards,
                                   void* o_partials, float* lses, void* workspace,
                                   int64_t workspace_bytes, void* stream);
+
+/* mla_decode_partial_shards for requests with different numbers of query
+ * tokens (varlen decode, as multi-token prediction produces: "GLM-5.2 vLLM
+ * Decode Context Parallelism", section "See why vLLM 0.26.0 fails" names the
+ * varlen-decode boundary the DCP backend must accept).  Request b has
+ * query_start_loc[b + 1] - query_start_loc[b] query tokens, query token t of
+ * it sits at position L_b - (its count) + t and attends positions up to it;
+ * a request may have none.
+ *   query_start_loc  [batch + 1] int32 device, first 0, last n_query_tokens,
+ *                    nondecreasing; otherwise the call raises
+ *                    MLA_DEVERR_QUERY in the workspace error word and its
+ *                    outputs are unspecified (every access stays in bounds)
+ *   q                [n_query_tokens][H][576]
+ *   topk_idx         [n_query_tokens][topk] or NULL (dense)
+ *   o_partials       [shard_count][n_query_tokens][H][512]
+ *   lses             [shard_count][n_query_tokens][H]
+ * desc->q_len bounds the call's size: n_query_tokens <= batch * q_len
+ * (else MLA_ERR_SHAPE), and mla_decode_workspace_size(desc, shard_count)
+ * sizes its workspace as for the fixed form.  Rows of o_partials / lses
+ * follow the query tokens; mla_lse_merge combines them as usual. */
+int32_t mla_decode_partial_shards_varlen(const mla_decode_desc* desc, const void* q,
+                                         const void* kv_pool, const int32_t* block_tables,
+                                         const int32_t* context_lens,
+                                         const int32_t* query_start_loc, int32_t n_query_tokens,
+                                         const int32_t* topk_idx, int32_t shard_begin,
+                                         int32_t shard_count, int32_t n_shards, void* o_partials,
+                                         float* lses, void* workspace, int64_t workspace_bytes,
+                                         void* stream);
 
 /* LSE merge of n_parts partials ("GLM-5.2 vLLM Decode Context Parallelism",
  * sections "See why vLLM 0.26.0 fails" and "Frequently asked questions"):

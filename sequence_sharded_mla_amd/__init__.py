@@ -13,7 +13,8 @@ import torch
 
 from . import _lib
 from ._lib import (MLA_BF16, MLA_F32, MLA_FP8_DS, MLA_DEVERR_BLOCK_TABLE,  # noqa: F401
-                   MLA_DEVERR_INDEX, MLA_DEVERR_SLOT, MLA_DEVERR_SCORES, MLADecodeDesc)
+                   MLA_DEVERR_INDEX, MLA_DEVERR_SLOT, MLA_DEVERR_SCORES, MLA_DEVERR_QUERY,
+                   MLADecodeDesc)
 
 DTYPE_CODES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8_ds": MLA_FP8_DS}
 LATENT = 512
@@ -102,6 +103,17 @@ def mla_decode_partial_shards(desc, q, kv_pool, block_tables, context_lens, topk
         ctypes.byref(desc), _ptr(q), _ptr(kv_pool), _ptr(block_tables), _ptr(context_lens),
         _ptr(topk_idx), shard_begin, shard_count, n_shards, _ptr(o_partials), _ptr(lses),
         _ptr(workspace), workspace.numel(), _stream(stream)), "mla_decode_partial_shards")
+
+
+def mla_decode_partial_shards_varlen(desc, q, kv_pool, block_tables, context_lens,
+                                     query_start_loc, topk_idx, shard_begin, shard_count, n_shards,
+                                     o_partials, lses, workspace, stream=None):
+    """q [n_q][H][576]; query_start_loc [B + 1] int32 -> o_partials / lses per shard."""
+    _check(_lib.load().mla_decode_partial_shards_varlen(
+        ctypes.byref(desc), _ptr(q), _ptr(kv_pool), _ptr(block_tables), _ptr(context_lens),
+        _ptr(query_start_loc), q.shape[0], _ptr(topk_idx), shard_begin, shard_count, n_shards,
+        _ptr(o_partials), _ptr(lses), _ptr(workspace), workspace.numel(), _stream(stream)),
+        "mla_decode_partial_shards_varlen")
 
 
 def mla_lse_merge(o_parts, lse_parts, o_out, lse_out=None, stream=None):

@@ -27,6 +27,7 @@ MLA_DEVERR_BLOCK_TABLE = 1
 MLA_DEVERR_INDEX = 2
 MLA_DEVERR_SLOT = 4
 MLA_DEVERR_SCORES = 8
+MLA_DEVERR_QUERY = 16
 
 
 class MLADecodeDesc(ctypes.Structure):
@@ -62,6 +63,8 @@ SIGNATURES = {
                                   _i64, _vp]),
     "mla_decode_partial_shards": (_i32, [_pdesc, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
                                          _vp, _vp, _i64, _vp]),
+    "mla_decode_partial_shards_varlen": (_i32, [_pdesc, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                                _i32, _vp, _vp, _vp, _i64, _vp]),
     "mla_lse_merge": (_i32, [_i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp]),
     "mla_localize_indices": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp]),
     "mla_dcp_slot_mapping": (_i32, [_vp, _vp, _i64, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _vp,

@@ -21,14 +21,17 @@ int32_t launch_status() {
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_DEVICE;
 }
 
+// qsl: null (q_len query tokens per request), or the varlen query offsets
+// [batch + 1] with n_q query tokens in all.
 int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool,
                     const int32_t* block_tables, const int32_t* context_lens,
                     const int32_t* topk_idx, int32_t shard_begin, int32_t shard_count,
                     int32_t n_shards, void* o, float* lse, void* ws, int64_t ws_bytes,
-                    void* stream) {
+                    void* stream, const int32_t* qsl = nullptr, int32_t n_q = -1) {
     Plan plan;
-    int32_t st = make_plan(d, shard_count, &plan);
+    int32_t st = make_plan(d, shard_count, &plan, n_q);
     if (st != MLA_OK) return st;
+    if (qsl && (reinterpret_cast<uintptr_t>(qsl) & 3u)) return MLA_ERR_ALIGN;
     if (n_shards < 1 || shard_begin < 0 || shard_begin + shard_count > n_shards)
         return MLA_ERR_SHARD;
     if (!q || !kv_pool || !block_tables || !context_lens || !o || !lse || !ws) return MLA_ERR_NULL;
@@ -38,7 +41,7 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
         (reinterpret_cast<uintptr_t>(lse) & 3u))
         return MLA_ERR_ALIGN;
     if (ws_bytes < plan.ws_bytes) return MLA_ERR_WORKSPACE;
-    if (d->batch == 0) return MLA_OK;
+    if (d->batch == 0 || plan.n_q == 0) return MLA_OK;
 
     DecodeParams p{};
     p.q = q;
@@ -61,6 +64,8 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     p.row_bytes = int32_t(row_bytes(d->kv_dtype));
     p.B = d->batch;
     p.Tq = d->q_len;
+    p.n_q = plan.n_q;
+    if (qsl) p.qmap = reinterpret_cast<const int32_t*>(w + plan.qmap_off);
     p.H = d->num_heads;
     p.max_blocks = d->max_blocks;
     p.topk = d->topk;
@@ -72,6 +77,13 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     p.scale = d->softmax_scale;
 
     hipStream_t s = as_stream(stream);
+    if (qsl) {
+        int64_t blocks = (plan.n_q + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        hipLaunchKernelGGL(qmap_kernel, dim3(uint32_t(blocks)), dim3(256), 0, s, qsl, d->batch, plan.n_q,
+                           reinterpret_cast<int32_t*>(w + plan.qmap_off), p.err);
+        if ((st = launch_status()) != MLA_OK) return st;
+    }
     if (plan.planned) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p, plan.target,
                            reinterpret_cast<int32_t*>(w), reinterpret_cast<int32_t*>(w + plan.items_off),
@@ -227,6 +239,22 @@ int32_t mla_decode_partial_shards(const mla_decode_desc* desc, const void* q,
     return mla::decode_impl(desc, q, kv_pool, block_tables, context_lens, topk_idx, shard_begin,
                             shard_count, n_shards, o_partials, lses, workspace, workspace_bytes,
                             stream);
+}
+
+int32_t mla_decode_partial_shards_varlen(const mla_decode_desc* desc, const void* q,
+                                         const void* kv_pool, const int32_t* block_tables,
+                                         const int32_t* context_lens,
+                                         const int32_t* query_start_loc, int32_t n_query_tokens,
+                                         const int32_t* topk_idx, int32_t shard_begin,
+                                         int32_t shard_count, int32_t n_shards, void* o_partials,
+                                         float* lses, void* workspace, int64_t workspace_bytes,
+                                         void* stream) {
+    if (!desc) return MLA_ERR_NULL;
+    if (n_query_tokens < 0) return MLA_ERR_SHAPE;
+    if (!query_start_loc && desc->batch > 0 && n_query_tokens > 0) return MLA_ERR_NULL;
+    return mla::decode_impl(desc, q, kv_pool, block_tables, context_lens, topk_idx, shard_begin,
+                            shard_count, n_shards, o_partials, lses, workspace, workspace_bytes,
+                            stream, query_start_loc, n_query_tokens);
 }
 
 int32_t mla_lse_merge(int32_t n_parts, int64_t rows, int32_t dv, int32_t part_dtype,

@@ -111,7 +111,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         (const __attribute__((address_space(4))) int32_t*)bt;
 
     const int32_t L = p.context_lens[id.b];
-    int32_t visible = L - p.Tq + id.t + 1;
+    int32_t visible = L - id.qlen + id.t + 1;
     if (visible < 0) visible = 0;
 
     // ---- the tokens this workgroup attends ---------------------------------
@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         // Compact the entries this shard owns, in entry order: wave w scans
         // its own slice of the list (ballot + popcount, no barrier), then
         // moves its owned entries down to their final position.
-        const int32_t* idx = p.topk_idx + (size_t(id.b) * p.Tq + id.t) * p.topk;
+        const int32_t* idx = p.topk_idx + size_t(id.qi) * p.topk;
         const int32_t slice = (p.topk + NW - 1) / NW;
         const int32_t e_begin = wave * slice;
         const int32_t e_end = min(p.topk, e_begin + slice);
@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     const int qr_sw = (head >> 1) & 7;
     {
         const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
-            static_cast<const uint16_t*>(p.q) + ((size_t(id.b) * p.Tq + id.t) * p.H + head) * kDk);
+            static_cast<const uint16_t*>(p.q) + (size_t(id.qi) * p.H + head) * kDk);
 #pragma unroll
         for (int ks = 0; ks < kQLatSteps; ++ks) qf[ks] = qrow[4 * (ks >> 1) + 2 * half + (ks & 1)];
         // rope part in LDS; each wave writes and later reads only its own heads

@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
 
     // ---- token range of this chunk ---------------------------------------
     const int32_t L = p.context_lens[id.b];
-    int32_t visible = L - p.Tq + id.t + 1;
+    int32_t visible = L - id.qlen + id.t + 1;
     if (visible < 0) visible = 0;
     int32_t local = dev_local_len(visible, s, p.n_shards);
     if ((local + kBlock - 1) / kBlock > p.max_blocks) {
@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     const int qr_sw = (head >> 1) & 7;
     {
         const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
-            static_cast<const uint16_t*>(p.q) + ((size_t(id.b) * p.Tq + id.t) * p.H + head) * kDk);
+            static_cast<const uint16_t*>(p.q) + (size_t(id.qi) * p.H + head) * kDk);
 #pragma unroll
         for (int ks = 0; ks < kQLatSteps; ++ks) qf[ks] = qrow[2 * ks + half];
 #pragma unroll

@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams p) {
 
     // query heads h0 .. h0+15 of (b, t) as float32
     {
-        const size_t qbase = ((size_t(id.b) * p.Tq + id.t) * p.H + h0) * kDk;
+        const size_t qbase = (size_t(id.qi) * p.H + h0) * kDk;
         for (int i = tid; i < kHeads * kDk; i += kThreads) {
             float v;
             if (KV == MLA_F32) v = static_cast<const float*>(p.q)[qbase + i];
@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams p) {
     for (int i = 0; i < 32; ++i) acc[i] = 0.f;
 
     const int32_t L = p.context_lens[id.b];
-    int32_t visible = L - p.Tq + id.t + 1;  // positions this query token sees
+    int32_t visible = L - id.qlen + id.t + 1;  // positions this query token sees
     if (visible < 0) visible = 0;
 
     if (p.topk == 0) {
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams p) {
             if (c > 0) tile_step<KV>(p, sm, c, m, l, acc);
         }
     } else {
-        const int32_t* idx = p.topk_idx + (size_t(id.b) * p.Tq + id.t) * p.topk;
+        const int32_t* idx = p.topk_idx + size_t(id.qi) * p.topk;
         const int lane = tid & 63, wave = tid >> 6;
         for (int32_t e0 = 0; e0 < p.topk; e0 += kListCap) {
             const int32_t e = e0 + tid;

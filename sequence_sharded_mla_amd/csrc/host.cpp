@@ -54,17 +54,25 @@ static int32_t plan_target(const mla_decode_desc* d) {
     return 512;
 }
 
-int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan) {
+int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan, int32_t n_q) {
     int32_t st = validate_desc(d);
     if (st != MLA_OK) return st;
     if (shard_count < 1 || shard_count > 4096) return MLA_ERR_SHARD;
+    const int64_t bound = int64_t(d->batch) * d->q_len;  // the most query tokens a call can have
+    if (n_q < 0) n_q = int32_t(bound);
+    if (n_q > bound) return MLA_ERR_SHAPE;
     Plan p;
-    p.rows = int32_t(int64_t(shard_count) * d->batch * d->q_len);
+    p.n_q = n_q;
+    p.rows = int32_t(int64_t(shard_count) * n_q);
     // a row holds at most max_blocks * 64 local tokens; when that fits in one
     // chunk of the smallest size, every row is one item and no plan is needed
     p.planned = d->topk == 0 && int64_t(d->max_blocks) * kBlock > kChunkMin;
     p.items_max = p.rows;
     int64_t off = kWsHeader;
+    // per query token (request, index in it, its query count, 0), filled for
+    // calls with a query count per request
+    p.qmap_off = off;
+    off = align_up(off + int64_t(n_q) * 16, 256);
     if (p.planned) {
         p.target = plan_target(d);
         // items per row <= local / chunk + 1 and sum(local) / chunk <= target

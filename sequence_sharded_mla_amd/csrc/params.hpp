@@ -7,13 +7,15 @@
 namespace mla {
 
 struct DecodeParams {
-    const void* q;               // [B][Tq][H][576] f32 or bf16
+    const void* q;               // [n_q][H][576] f32 or bf16 (n_q = B*Tq, or the varlen count)
     const uint8_t* kv;           // [pool_blocks][64][row_bytes]
     const int32_t* block_tables; // [shard_count][B][max_blocks]
     const int32_t* context_lens; // [B]
-    const int32_t* topk_idx;     // [B][Tq][topk] or null
-    void* o_out;                 // [shard_count][B*Tq][H][512] out dtype
-    float* lse_out;              // [shard_count][B*Tq][H]
+    const int32_t* topk_idx;     // [n_q][topk] or null
+    const int32_t* qmap;         // varlen: [n_q][4] request, token index in it, its query count, 0;
+                                 // null: Tq tokens per request
+    void* o_out;                 // [shard_count][n_q][H][512] out dtype
+    float* lse_out;              // [shard_count][n_q][H]
     void* ws_o;                  // partials of split rows: [slots][H][512] out dtype
     float* ws_lse;               // [slots][H]
     const int32_t* items;        // [n][4] row, chunk, partial slot (-1: whole row), 0;
@@ -24,6 +26,7 @@ struct DecodeParams {
     int64_t pool_blocks;
     int32_t row_bytes;
     int32_t B, Tq, H, max_blocks, topk;
+    int32_t n_q;                 // query tokens per shard: B * Tq, or the varlen count
     int32_t shard_begin, shard_count, n_shards;
     int32_t rows;
     int32_t out_dtype;
@@ -31,19 +34,31 @@ struct DecodeParams {
 };
 
 // One unit of work: a (shard, request, query token) row, or a chunk of the
-// row's local tokens.
+// row's local tokens.  qi indexes the query token in q, topk_idx and the
+// outputs; qlen is its request's query count (query token t of a request
+// with context L sits at position L - qlen + t).
 struct RowId {
     int32_t s_rel, b, t, row;
+    int32_t qi, qlen;
     int32_t chunk;      // chunk index within the row
     int32_t slot;       // partial slot, or -1 when the item covers the whole row
     int32_t chunk_tok;  // tokens per chunk (0: the whole row)
 };
 
 __device__ __forceinline__ void split_row(const DecodeParams& p, RowId& r) {
-    r.t = r.row % p.Tq;
-    const int32_t bt = r.row / p.Tq;
-    r.b = bt % p.B;
-    r.s_rel = bt / p.B;
+    r.s_rel = r.row / p.n_q;
+    r.qi = r.row - r.s_rel * p.n_q;
+    if (!p.qmap) {
+        r.t = r.qi % p.Tq;
+        r.b = r.qi / p.Tq;
+        r.qlen = p.Tq;
+    } else {
+        const __attribute__((address_space(4))) int32_t* m =
+            (const __attribute__((address_space(4))) int32_t*)p.qmap + 4 * size_t(r.qi);
+        r.b = m[0];
+        r.t = m[1];
+        r.qlen = m[2];
+    }
 }
 
 // Work item of workgroup `idx`; false for a workgroup past the last item (the

@@ -27,12 +27,14 @@ constexpr int64_t kWsHeader = 256;  // int32 [0] device error word, [1] item cou
 constexpr int32_t kChunkMin = 4096;  // fewest local tokens per chunk of a split row
 
 struct Plan {
-    int32_t rows = 0;           // shard_count * B * Tq
+    int32_t n_q = 0;            // query tokens per shard (B * Tq, or the varlen count)
+    int32_t rows = 0;           // shard_count * n_q
     bool planned = false;       // dense rows that may split: device plan + combine
     int32_t target = 0;         // items the device plan aims for
     int32_t items_max = 0;      // workgroups to launch (an upper bound on items)
     int32_t slots = 0;          // partial slots of split rows
     int64_t ws_bytes = kWsHeader; // workspace the call needs
+    int64_t qmap_off = 0;       // int32 [n_q][4]
     int64_t items_off = 0;      // int32 [items_max][4]
     int64_t row_info_off = 0;   // int32 [rows][2]
     int64_t ws_o_off = 0;       // out dtype [slots][H][512]
@@ -45,7 +47,8 @@ int32_t local_len(int32_t context_len, int32_t shard_id, int32_t n_shards);
 // Validates desc (and shard_count >= 1) and fills the plan.  Returns MLA_OK or
 // the status code of the first failed check.
 int32_t validate_desc(const mla_decode_desc* d);
-int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan);
+// n_q: query tokens per shard, at most batch * q_len (-1: batch * q_len).
+int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan, int32_t n_q = -1);
 
 bool aligned16(const void* p);
 

@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(DecodeParams p, int3
         RowId r;
         r.row = row;
         split_row(p, r);
-        int32_t visible = p.context_lens[r.b] - p.Tq + r.t + 1;
+        int32_t visible = p.context_lens[r.b] - r.qlen + r.t + 1;
         if (visible < 0) visible = 0;
         const int32_t local = dev_local_len(visible, p.shard_begin + r.s_rel, p.n_shards);
         return local > cap ? cap : local;
@@ -333,6 +333,41 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(int n, int64_t rows, con
     merge_wave<T>(n, o + size_t(row) * kLatent, size_t(rows) * kLatent, lse + row, size_t(rows),
                   out, out_dtype, size_t(row) * kLatent, lse_out ? lse_out + row : nullptr,
                   threadIdx.x & 63);
+}
+
+// Varlen query map: query token i of a call whose request b holds tokens
+// qsl[b] .. qsl[b + 1] - 1 -> (b, index t in the request, the request's
+// query count, 0).  Offsets that are not a partition of [0, n_q) set
+// MLA_DEVERR_QUERY; a token the search cannot place inside its request then
+// gets a query count so large that it sees no position.  Every read stays in
+// qsl[0 .. B] and every write in qmap[0 .. 4 n_q).
+__global__ void qmap_kernel(const int32_t* qsl, int32_t B, int32_t n_q, int32_t* qmap, uint32_t* err) {
+    const int32_t stride = gridDim.x * blockDim.x;
+    const int32_t first = blockIdx.x * blockDim.x + threadIdx.x;
+    if (first == 0 && (qsl[0] != 0 || qsl[B] != n_q)) raise_error(err, MLA_DEVERR_QUERY);
+    for (int32_t b = first; b < B; b += stride)
+        if (qsl[b] > qsl[b + 1]) raise_error(err, MLA_DEVERR_QUERY);
+    for (int32_t i = first; i < n_q; i += stride) {
+        int32_t lo = 0, hi = B - 1;  // largest b with qsl[b] <= i, for sorted offsets
+        while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) >> 1;
+            if (qsl[mid] <= i) lo = mid;
+            else hi = mid - 1;
+        }
+        const int64_t start = qsl[lo], end = qsl[lo + 1];
+        int32_t* m = qmap + 4 * size_t(i);
+        if (start < 0 || end > n_q || i < start || i >= end) {
+            raise_error(err, MLA_DEVERR_QUERY);
+            m[0] = 0;
+            m[1] = 0;
+            m[2] = INT32_MAX / 2;
+        } else {
+            m[0] = lo;
+            m[1] = int32_t(i - start);
+            m[2] = int32_t(end - start);
+        }
+        m[3] = 0;
+    }
 }
 
 __global__ void localize_kernel(const int32_t* g, int64_t count, int32_t shard, int32_t n,

@@ -165,6 +165,32 @@ def test_empty_batch_is_a_no_op(lib):
     assert call_shards(lib, good_desc(batch=0)) == 0
 
 
+def call_varlen(lib, desc, n_q, qsl=FAKE, **kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, ctx=FAKE, topk=None, begin=0, count=8, n=8, o=FAKE,
+             lse=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.mla_decode_partial_shards_varlen(
+        ctypes.byref(desc), v(a["q"]), v(a["kv"]), v(a["bt"]), v(a["ctx"]), v(qsl), n_q,
+        v(a["topk"]), a["begin"], a["count"], a["n"], v(a["o"]), v(a["lse"]), v(a["ws"]),
+        a["ws_bytes"], None)
+
+
+def test_varlen_checks(lib):
+    d = good_desc(q_len=3)                       # at most 4 * 3 query tokens
+    assert call_varlen(lib, d, -1) == _lib.MLA_ERR_SHAPE
+    assert call_varlen(lib, d, 13) == _lib.MLA_ERR_SHAPE
+    assert call_varlen(lib, d, 5, qsl=None) == _lib.MLA_ERR_NULL
+    assert call_varlen(lib, d, 5, qsl=FAKE + 2) == _lib.MLA_ERR_ALIGN
+    assert call_varlen(lib, d, 5, q=None) == _lib.MLA_ERR_NULL
+    assert call_varlen(lib, d, 5, begin=1) == _lib.MLA_ERR_SHARD
+    assert call_varlen(lib, d, 5, ws_bytes=100) == _lib.MLA_ERR_WORKSPACE
+    assert call_varlen(lib, d, 0) == 0           # no query tokens: nothing to do
+    assert call_varlen(lib, good_desc(batch=0), 0, qsl=None) == 0
+    assert lib.mla_decode_partial_shards_varlen(None, *([None] * 5), 0, *([None]), 0, 1, 1,
+                                                None, None, None, 0, None) == _lib.MLA_ERR_NULL
+
+
 def test_single_shard_entry_checks(lib):
     d = good_desc()
     v = ctypes.c_void_p

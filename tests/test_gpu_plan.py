@@ -1,6 +1,6 @@
 """The device plan of a dense step, read back from the workspace.
 
-White-box: the workspace layout (256-B header, items, row_info) is the
+White-box: the workspace layout (256-B header, query map, items, row_info) is the
 library's own.  For each row (shard, request, query token) the plan must
 list its chunks exactly once, with the chunk size the total work gives, a
 consecutive block of partial slots for each split row, and the items
@@ -73,8 +73,9 @@ def test_plan_lists_every_chunk_once_longest_first(name, kw):
     n_items = int(k.sum())
     assert hdr[1] == n_items
     items_max = rows + target
-    items = ws[256:256 + items_max * 16].view(np.int32).reshape(items_max, 4)[:n_items]
-    ri_off = align(256 + items_max * 16)
+    items_off = align(256 + B * Tq * 16)          # after the per-token query map
+    items = ws[items_off:items_off + items_max * 16].view(np.int32).reshape(items_max, 4)[:n_items]
+    ri_off = align(items_off + items_max * 16)
     row_info = ws[ri_off:ri_off + rows * 8].view(np.int32).reshape(rows, 2)
     assert np.array_equal(row_info[:, 1], k)
     # every (row, chunk) once
