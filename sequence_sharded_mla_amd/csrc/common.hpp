@@ -22,6 +22,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return uint16_t(u >> 16);
 }
 
+// Two float32 -> packed bfloat16 (a in the low half), round-to-nearest-even,
+// in one hardware conversion (v_cvt_pk_bf16_f32).  The output paths use it;
+// the cache write keeps f32_to_bf16, whose result on every input is fixed
+// by its definition above.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // OCP E4M3FN code -> float32 from the bit fields: bias 7, subnormals
 // m * 2^-9, S.1111.111 = NaN, no infinities.
 __device__ __forceinline__ float e4m3fn_to_f32(uint32_t c) {

@@ -114,6 +114,22 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     int32_t visible = L - id.qlen + id.t + 1;
     if (visible < 0) visible = 0;
 
+    // ---- query fragments: latent in registers (paired-step order), rope
+    // part through LDS.  Issued first, so that their latency overlaps the
+    // sparse compaction's loads.
+    bf16x8 qf[kQLatSteps];
+    bf16x8 qrope_r[4];
+    const int qr_off = head * (kRope * 2);
+    const int qr_sw = (head >> 1) & 7;
+    {
+        const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
+            static_cast<const uint16_t*>(p.q) + (size_t(id.qi) * p.H + head) * kDk);
+#pragma unroll
+        for (int ks = 0; ks < kQLatSteps; ++ks) qf[ks] = qrow[4 * (ks >> 1) + 2 * half + (ks & 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) qrope_r[u] = qrow[2 * (kQLatSteps + u) + half];
+    }
+
     // ---- the tokens this workgroup attends ---------------------------------
     int32_t tok0 = 0, tok1 = 0;  // dense: local token range; sparse: list range
     int total_owned = 0;
@@ -130,6 +146,22 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         // Compact the entries this shard owns, in entry order: wave w scans
         // its own slice of the list (ballot + popcount, no barrier), then
         // moves its owned entries down to their final position.
+        // The block-table row goes to LDS (the third ring slot is free until
+        // the ring starts) with direct loads issued beside the index loads,
+        // so one memory round trip covers the query, the indices and the
+        // table; a row wider than the slot is looked up in memory instead.
+        const bool bt_lds = p.max_blocks <= kCodesB / 4;
+        const uint32_t bt_stage = lds_addr(sm.codes[kRingF - 1]);
+        if (bt_lds) {
+            const int nk = (p.max_blocks + NW * 64 - 1) / (NW * 64);
+            const uint32_t m_bt = __builtin_amdgcn_readfirstlane(bt_stage + wv * 256);
+            for (int k = 0; k < nk; ++k) {
+                const int e = k * NW * 64 + wave * 64 + lane;
+                dma4_at<0>(bt, 4 * (e < p.max_blocks ? e : p.max_blocks - 1),
+                           __builtin_amdgcn_readfirstlane(m_bt + k * NW * 256));
+            }
+        }
+        const MLA_LDS int32_t* bt_l = (const MLA_LDS int32_t*)sm.codes[kRingF - 1];
         const int32_t* idx = p.topk_idx + size_t(id.qi) * p.topk;
         const int32_t slice = (p.topk + NW - 1) / NW;
         const int32_t e_begin = wave * slice;
@@ -144,6 +176,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
             const int32_t e = e_begin + k * 64 + lane;
             gv[k] = e < e_end ? idx[e] : -1;
         }
+        if (bt_lds) {
+            wait_vm<0>();  // this wave's table loads (and the query and index loads)
+            __syncthreads();
+        }
         int32_t row[kSteps];
 #pragma unroll
         for (int k = 0; k < kSteps; ++k) {
@@ -153,7 +189,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
                 raise_error(p.err, MLA_DEVERR_INDEX);
             } else if (g >= 0 && g % p.n_shards == s) {
                 const int32_t j = g / p.n_shards;
-                row[k] = j / kBlock < p.max_blocks ? bt[j / kBlock] : -1;  // block id for now
+                // block id for now
+                row[k] = j / kBlock >= p.max_blocks ? -1 : bt_lds ? bt_l[j / kBlock] : bt[j / kBlock];
                 row[k] = row[k] >= 0 && row[k] < p.pool_blocks ? row[k] * kBlock + (j % kBlock) : -2;
             }
         }
@@ -198,22 +235,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     // rounds: padding sub-tiles are zero rows with every score masked
     const int n_pad = (n_sub + kRingF - 1) / kRingF * kRingF;
 
-    // ---- query fragments (registers): latent in paired-step order, rope ----
-    bf16x8 qf[kQLatSteps];
-    const int qr_off = head * (kRope * 2);
-    const int qr_sw = (head >> 1) & 7;
-    {
-        const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
-            static_cast<const uint16_t*>(p.q) + (size_t(id.qi) * p.H + head) * kDk);
+    // rope part in LDS; each wave writes and later reads only its own heads
 #pragma unroll
-        for (int ks = 0; ks < kQLatSteps; ++ks) qf[ks] = qrow[4 * (ks >> 1) + 2 * half + (ks & 1)];
-        // rope part in LDS; each wave writes and later reads only its own heads
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = 2 * u + half;
-            *(MLA_LDS bf16x8*)((MLA_LDS uint8_t*)sm.qrope + qr_off + ((c ^ qr_sw) << 4)) =
-                qrow[2 * (kQLatSteps + u) + half];
-        }
+    for (int u = 0; u < 4; ++u) {
+        const int c = 2 * u + half;
+        *(MLA_LDS bf16x8*)((MLA_LDS uint8_t*)sm.qrope + qr_off + ((c ^ qr_sw) << 4)) = qrope_r[u];
     }
     auto qread = [&](int u) -> bf16x8 {
         return *(const MLA_LDS bf16x8*)((const MLA_LDS uint8_t*)sm.qrope + qr_off +
@@ -510,19 +536,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     const bool direct = id.slot < 0;
     const size_t orow = direct ? size_t(id.row) * p.H + head : size_t(id.slot) * p.H + head;
     if (p.out_dtype == MLA_BF16) {
-        uint16_t* o = static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) + orow * kLatent;
-#pragma unroll
-        for (int mt = 0; mt < kDvTiles; ++mt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * mt + 8 * q4 + 4 * half;
-                uint2 w;
-                w.x = uint32_t(f32_to_bf16(acc[mt][4 * q4 + 0] * inv)) |
-                      (uint32_t(f32_to_bf16(acc[mt][4 * q4 + 1] * inv)) << 16);
-                w.y = uint32_t(f32_to_bf16(acc[mt][4 * q4 + 2] * inv)) |
-                      (uint32_t(f32_to_bf16(acc[mt][4 * q4 + 3] * inv)) << 16);
-                *reinterpret_cast<uint2*>(o + d) = w;
-            }
+        // staged through the ring's LDS once every wave is past its last read
+        constexpr int kPasses = NW == 2 ? 1 : 2;
+        constexpr int kWaveB = 32 * 1024 / kPasses;
+        static_assert(sizeof(sm) >= NW * kWaveB, "staging fits the LDS of the ring");
+        __syncthreads();
+        store_rows_bf16<kPasses>(acc, inv, (MLA_LDS uint8_t*)&sm + wave * kWaveB,
+                                    static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) +
+                                        (orow - col) * kLatent,
+                                    lane);
     } else {
         float* o = static_cast<float*>(direct ? p.o_out : p.ws_o) + orow * kLatent;
 #pragma unroll

@@ -437,19 +437,12 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     const bool direct = id.slot < 0;
     const size_t orow = direct ? size_t(id.row) * p.H + head : size_t(id.slot) * p.H + head;
     if (p.out_dtype == MLA_BF16) {
-        uint16_t* o = static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) + orow * kLatent;
-#pragma unroll
-        for (int mt = 0; mt < kDvTiles; ++mt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * mt + 8 * q4 + 4 * half;
-                uint2 w;
-                w.x = uint32_t(f32_to_bf16(acc[mt][4 * q4 + 0] * inv)) |
-                      (uint32_t(f32_to_bf16(acc[mt][4 * q4 + 1] * inv)) << 16);
-                w.y = uint32_t(f32_to_bf16(acc[mt][4 * q4 + 2] * inv)) |
-                      (uint32_t(f32_to_bf16(acc[mt][4 * q4 + 3] * inv)) << 16);
-                *reinterpret_cast<uint2*>(o + d) = w;
-            }
+        // staged through the ring's LDS once every wave is past its last read
+        static_assert(sizeof(sm) >= 4 * 32 * 1024, "staging fits the LDS of the ring");
+        __syncthreads();
+        store_rows_bf16<1>(acc, inv, (MLA_LDS uint8_t*)&sm + wave * 32 * 1024,
+                            static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) + (orow - col) * kLatent,
+                            lane);
     } else {
         float* o = static_cast<float*>(direct ? p.o_out : p.ws_o) + orow * kLatent;
 #pragma unroll

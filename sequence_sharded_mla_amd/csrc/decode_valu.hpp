@@ -232,7 +232,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams p) {
     } else {
         uint16_t* o = static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) + head * kLatent;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) o[tl + 16 * i] = f32_to_bf16(acc[i] * inv);
+        for (int i = 0; i < 32; ++i) o[tl + 16 * i] = uint16_t(bf16x2_rne(acc[i] * inv, 0.f));
     }
     if (tl == 0) (direct ? p.lse_out : p.ws_lse)[head] = lse;
 }

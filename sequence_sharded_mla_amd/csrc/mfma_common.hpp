@@ -159,6 +159,19 @@ __device__ __forceinline__ void dma16_v_at(const void* gptr, uint32_t lds_base) 
         : "memory", "m0", "scc");
 }
 
+// One wave-wide 4-byte direct-to-LDS load: lane i copies 4 bytes from
+// gbase + voff(i) to LDS byte lds_base + IMM + 4 i.
+template <int IMM>
+__device__ __forceinline__ void dma4_at(const void* gbase, int voff, uint32_t lds_base) {
+    asm volatile(
+        "s_add_u32 m0, %2, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, %1"
+        :
+        : "v"(voff), "s"(gbase), "s"(lds_base), "n"(IMM)
+        : "memory", "m0", "scc");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return uint32_t(reinterpret_cast<uintptr_t>((const MLA_LDS void*)p));
 }
@@ -192,6 +205,49 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float a) {
             : "+a"(x), "=&v"(tmp)
             : "v"(a));
         acc[e] = x;
+    }
+}
+
+// The bf16 output rows of one wave (32 heads x 512 values, O = acc * inv)
+// leave through LDS so that global stores write whole 512-byte or 1 KB runs
+// of head rows: acc[mt][4 q4 + e] holds dimension 32 mt + 8 q4 + 4 half + e
+// of head `col`.  PASSES splits the dimensions (1: all 512 at once, 32 KB of
+// LDS per wave; 2: 256 at a time, 16 KB).  `stage` is this wave's region;
+// 16-byte chunk c of staged row r sits at chunk c ^ r, so the 8-byte writes
+// of one instruction spread over the banks and a read returns contiguous
+// row bytes.  Every lane takes part in every step (no lane-dependent
+// branch), and LDS accesses of one wave complete in order, so the passes
+// need no barrier; the caller makes sure no other wave still reads the
+// region.  `out` points at the wave's first head row.
+template <int PASSES>
+__device__ __forceinline__ void store_rows_bf16(const f32x16 (&acc)[kDvTiles], float inv,
+                                                MLA_LDS uint8_t* stage, uint16_t* out, int lane) {
+    static_assert(PASSES == 1 || PASSES == 2, "dimension passes");
+    constexpr int kRB = 1024 / PASSES;        // bytes of a staged row
+    constexpr int kCh = kRB / 16;             // 16-byte chunks per staged row
+    constexpr int kMt = kDvTiles / PASSES;    // output tiles per pass
+    constexpr int kRowsPerOp = 64 / kCh;      // staged rows per 64-lane read
+    const int col = lane & 31, half = lane >> 5;
+    MLA_LDS uint8_t* wrow = stage + col * kRB + 8 * half;
+    const int rsub = lane / kCh, j = lane % kCh;
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+#pragma unroll
+        for (int mt = 0; mt < kMt; ++mt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x16& a = acc[pass * kMt + mt];
+                i32x2 w;
+                w[0] = int(bf16x2_rne(a[4 * q4 + 0] * inv, a[4 * q4 + 1] * inv));
+                w[1] = int(bf16x2_rne(a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv));
+                *(MLA_LDS i32x2*)(wrow + (((4 * mt + q4) ^ col) << 4)) = w;
+            }
+#pragma unroll
+        for (int k = 0; k < 32 / kRowsPerOp; ++k) {
+            const int r = k * kRowsPerOp + rsub;
+            const i32x4 v = *(const MLA_LDS i32x4*)(stage + r * kRB + ((j ^ r) << 4));
+            *reinterpret_cast<i32x4*>(out + size_t(r) * kLatent + pass * (kLatent / PASSES) + 8 * j) = v;
+        }
     }
 }
 

@@ -44,10 +44,10 @@ __device__ __forceinline__ void store8(void* base, int dtype, size_t i, const fl
         *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
     } else {
         uint4 x;
-        x.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
-        x.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
-        x.z = uint32_t(f32_to_bf16(v[4])) | (uint32_t(f32_to_bf16(v[5])) << 16);
-        x.w = uint32_t(f32_to_bf16(v[6])) | (uint32_t(f32_to_bf16(v[7])) << 16);
+        x.x = bf16x2_rne(v[0], v[1]);
+        x.y = bf16x2_rne(v[2], v[3]);
+        x.z = bf16x2_rne(v[4], v[5]);
+        x.w = bf16x2_rne(v[6], v[7]);
         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + i) = x;
     }
 }
