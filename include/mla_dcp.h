@@ -139,7 +139,8 @@ int32_t mla_decode_workspace_size(const mla_decode_desc* desc, int32_t shard_cou
  * the causal prefix; sparse: owned entries of topk_idx[b][t]), writing the
  * normalised partial output and its LSE ("GLM-5.2 vLLM Decode Context
  * Parallelism", sections "See why vLLM 0.26.0 fails" and "Separate the backend
- * merge from stable").  topk_idx must be NULL when desc->topk == 0 and
+ * merge from stable").  1 <= n_shards <= 4096 and 0 <= shard_id < n_shards
+ * (else MLA_ERR_SHARD).  topk_idx must be NULL when desc->topk == 0 and
  * non-NULL otherwise.  workspace: device memory of workspace_bytes >=
  * mla_decode_workspace_size(desc, 1); its first word is the sticky device
  * error word, the rest is scratch overwritten by the call. */

@@ -32,7 +32,7 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     int32_t st = make_plan(d, shard_count, &plan, n_q);
     if (st != MLA_OK) return st;
     if (qsl && (reinterpret_cast<uintptr_t>(qsl) & 3u)) return MLA_ERR_ALIGN;
-    if (n_shards < 1 || shard_begin < 0 || shard_begin + shard_count > n_shards)
+    if (n_shards < 1 || n_shards > 4096 || shard_begin < 0 || shard_begin + shard_count > n_shards)
         return MLA_ERR_SHARD;
     if (!q || !kv_pool || !block_tables || !context_lens || !o || !lse || !ws) return MLA_ERR_NULL;
     if (d->topk > 0 && !topk_idx) return MLA_ERR_NULL;

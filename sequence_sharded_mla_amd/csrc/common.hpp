@@ -55,6 +55,15 @@ __device__ __forceinline__ int32_t dev_local_len(int32_t L, int32_t s, int32_t n
     return L > s ? (L - s + n - 1) / n : 0;
 }
 
+// floor(g / n) for 0 <= g < 2^31 and 1 <= n <= 4096, given inv = 1.0 / n in
+// float64.  g * inv lies within 2^-21 of g / n, and a quotient that is not an
+// integer is at least 1/n >= 2^-12 below the next integer, so truncating
+// g * inv + 2^-20 gives the exact floor (a handful of instructions instead of
+// an integer division by a runtime divisor).
+__device__ __forceinline__ int32_t div_by(int32_t g, double inv) {
+    return int32_t(fma(double(g), inv, 0x1p-20));
+}
+
 __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bit) {
     atomicOr(err, bit);
 }

@@ -180,15 +180,16 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
             wait_vm<0>();  // this wave's table loads (and the query and index loads)
             __syncthreads();
         }
+        const double inv_n = 1.0 / double(p.n_shards);
         int32_t row[kSteps];
 #pragma unroll
         for (int k = 0; k < kSteps; ++k) {
             const int32_t g = gv[k];
+            const int32_t j = div_by(g < 0 ? 0 : g, inv_n);  // local index if owned
             row[k] = -1;
             if (g >= visible) {
                 raise_error(p.err, MLA_DEVERR_INDEX);
-            } else if (g >= 0 && g % p.n_shards == s) {
-                const int32_t j = g / p.n_shards;
+            } else if (g >= 0 && g - j * p.n_shards == s) {
                 // block id for now
                 row[k] = j / kBlock >= p.max_blocks ? -1 : bt_lds ? bt_l[j / kBlock] : bt[j / kBlock];
                 row[k] = row[k] >= 0 && row[k] < p.pool_blocks ? row[k] * kBlock + (j % kBlock) : -2;

@@ -66,7 +66,18 @@ __device__ __forceinline__ void split_row(const DecodeParams& p, RowId& r) {
 // the workgroup and go through the scalar cache.
 __device__ __forceinline__ bool work_item(const DecodeParams& p, int32_t idx, RowId& r) {
     if (!p.items) {
+        // Workgroups are dealt to the eight XCDs round robin (workgroup i on
+        // XCD i mod 8), each with its own L2.  Rows are numbered shard-major
+        // (row = s_rel * n_q + qi); XCD x instead takes the rows of a block
+        // of query tokens in token-major order, so the shards of one token
+        // run together on one XCD and read its query (and index list) from
+        // that L2.
         r.row = idx;
+        if (p.rows % 8 == 0) {
+            const int32_t u = (idx % 8) * (p.rows / 8) + idx / 8;  // token-major row
+            const int32_t qi = u / p.shard_count;
+            r.row = (u - qi * p.shard_count) * p.n_q + qi;
+        }
         r.chunk = 0;
         r.slot = -1;
         r.chunk_tok = 0;

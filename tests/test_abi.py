@@ -141,6 +141,7 @@ def call_shards(lib, desc, **kw):
     (dict(begin=-1), _lib.MLA_ERR_SHARD),
     (dict(count=0), _lib.MLA_ERR_SHARD),
     (dict(n=0, count=1), _lib.MLA_ERR_SHARD),
+    (dict(n=4097, count=1), _lib.MLA_ERR_SHARD),
     (dict(q=FAKE + 8), _lib.MLA_ERR_ALIGN),
     (dict(kv=FAKE + 4), _lib.MLA_ERR_ALIGN),
     (dict(o=FAKE + 2), _lib.MLA_ERR_ALIGN),
