@@ -432,20 +432,22 @@ __device__ bool select_one_pass(SelectShared& sh, SelList& buf, const Src& src, 
     // raw scores stay in registers (4 bytes each) until they are used
     uint32_t d_min = 0;
     constexpr int V = Src::V;
-    const int64_t groups = (n + V - 1) / V;
+    // local rows hold at most kMaxLocal positions: 32-bit indices
+    const int32_t n32 = int32_t(n);
+    const int32_t groups = (n32 + V - 1) / V;
     const int lane = threadIdx.x & 63;
-    for (int64_t base = 0; base < groups; base += int64_t(kThreads) * U) {
-        const int64_t g0 = base + threadIdx.x;
+    for (int32_t base = 0; base < groups; base += kThreads * U) {
+        const int32_t g0 = base + int32_t(threadIdx.x);
         float x[U][V];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t g = g0 + int64_t(u) * kThreads;
+            const int32_t g = g0 + u * kThreads;
             if (g < groups) src.load(g, x[u]);
         }
         if (base == 0 && n > kBuf) {
             // the sample's load goes out behind the first batch's, so the
             // wait for it costs no extra round trip
-            const int64_t i = int64_t(threadIdx.x) * (n / kThreads);
+            const int32_t i = int32_t(threadIdx.x) * (n32 / kThreads);
             atomicAdd(&sh.hist[uint32_t(make_key(row[i], uint32_t(i)) >> 52)], 1u);
             __syncthreads();
             // the kept share of the sample plus a few: the digit's bins are
@@ -470,8 +472,8 @@ __device__ bool select_one_pass(SelectShared& sh, SelList& buf, const Src& src, 
         }
         // digit of element (u, v), or 0 when it is past the row
         auto digit = [&](int u, int v) -> uint32_t {
-            const int64_t i = (g0 + int64_t(u) * kThreads) * V + v;
-            return i < n ? score_bits(x[u][v]) >> 20 : 0u;
+            const int32_t i = (g0 + u * kThreads) * V + v;
+            return i < n32 ? score_bits(x[u][v]) >> 20 : 0u;
         };
         uint32_t cnt = 0;
 #pragma unroll
@@ -482,7 +484,7 @@ __device__ bool select_one_pass(SelectShared& sh, SelList& buf, const Src& src, 
                 // only digits >= D are counted: the K-th key's digit is found
                 // among them or the row takes the general path (d_min >= 1
                 // whenever past-the-row elements could pass)
-                if (d >= d_min && (d_min > 0 || (g0 + int64_t(u) * kThreads) * V + v < n)) {
+                if (d >= d_min && (d_min > 0 || (g0 + u * kThreads) * V + v < n32)) {
                     atomicAdd(&sh.hist[d], 1u);
                     ++cnt;
                 }
@@ -502,9 +504,9 @@ __device__ bool select_one_pass(SelectShared& sh, SelList& buf, const Src& src, 
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                const int64_t i = (g0 + int64_t(u) * kThreads) * V + v;
+                const int32_t i = (g0 + u * kThreads) * V + v;
                 const uint32_t d = digit(u, v);
-                if (!(d >= d_min && (d_min > 0 || i < n))) continue;
+                if (!(d >= d_min && (d_min > 0 || i < n32))) continue;
                 if (at < uint32_t(kBuf)) {
                     buf.sb[at] = score_bits(x[u][v]);
                     buf.idx[at] = uint32_t(i);
