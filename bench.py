@@ -77,6 +77,24 @@ def algorithmic_bytes(x, out_bytes=2, q_bytes=2):
     return step, decode_launch, tokens
 
 
+def shard_bytes(x, s, out_bytes=2, q_bytes=2):
+    """Algorithmic bytes of one shard's decode launch (what one DCP rank's
+    call moves): its owned KV rows, the query, the index lists, its partials."""
+    from sequence_sharded_mla_amd.layout import ROW_BYTES
+    sp = x.spec
+    B, Tq, H, N = sp.batch, sp.q_len, sp.heads, sp.n_shards
+    if x.topk_idx is None:
+        vis = [max(int(L) - Tq + j + 1, 0) for L in x.context_lens for j in range(Tq)]
+        tokens = int(sum((v - s + N - 1) // N if v > s else 0 for v in vis))
+        idx_bytes = 0
+    else:
+        g = x.topk_idx
+        tokens = int(((g >= 0) & (g % N == s)).sum())
+        idx_bytes = g.size * 4
+    return tokens * ROW_BYTES[sp.kv_dtype] + B * Tq * H * 576 * q_bytes + idx_bytes + \
+        B * Tq * H * (512 * out_bytes + 4), tokens
+
+
 def cpu_baseline(x, budget_s=10.0):
     """Time the float64 oracle (shard partials + merge) on whole requests."""
     from threadpoolctl import threadpool_info
@@ -438,6 +456,52 @@ def main():
     t_merge = np.array([e[1].elapsed_time(e[2]) for e in ev])
     assert mla_get_device_error(step.workspace) == 0
 
+    # Cold-cache series (not the timed region): a 1 GiB fill before every
+    # step evicts the 256 MB last-level cache, so no KV row of the previous
+    # step is served from it; only the events around the launches count.
+    evict = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = []
+    for i in range(K):
+        evict.fill_(i & 0xff)
+        a, b, c = ev[i]
+        a.record(stream)
+        step.partials()
+        b.record(stream)
+        step.merge()
+        c.record(stream)
+        torch.cuda.synchronize()
+        cold.append((a.elapsed_time(b), b.elapsed_time(c)))
+    cold = np.array(cold)
+    del evict
+    assert mla_get_device_error(step.workspace) == 0
+
+    # One shard's call, the launch one DCP rank makes for its share of the
+    # cache (shard 0, its own block table and workspace).
+    from sequence_sharded_mla_amd import alloc_workspace, mla_decode_partial
+    d = cache.desc
+    rows = d.batch * d.q_len
+    o1 = torch.empty((rows, d.num_heads, 512), dtype=step.o_partials.dtype, device="cuda")
+    l1 = torch.empty((rows, d.num_heads), dtype=torch.float32, device="cuda")
+    ws1 = alloc_workspace(d, 1)
+    bt0 = cache.block_tables[0].contiguous()
+
+    def one_shard():
+        mla_decode_partial(d, cache.q, cache.pool, bt0, cache.context_lens, cache.topk_idx, 0,
+                           cache.n_shards, o1, l1, ws1)
+    for _ in range(3):
+        one_shard()
+    torch.cuda.synchronize()
+    t_one = []
+    for i in range(K):
+        a, b, _ = ev[i]
+        a.record(stream)
+        one_shard()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t_one = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    assert mla_get_device_error(ws1) == 0
+    one_bytes, one_tokens = shard_bytes(x, 0, out_b, q_b)
+
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     part_ms = float(np.mean(t_part))
     achieved = launch_bytes / (part_ms * 1e-3) / 1e9
@@ -462,9 +526,20 @@ def main():
         "kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "algorithmic_bytes_per_step": int(step_bytes),
         "kernels_ms": {"decode_partials": round(part_ms, 4),
+                       "decode_partials_median": round(float(np.median(t_part)), 4),
                        "decode_partials_p10_p90": [round(float(np.percentile(t_part, 10)), 4),
                                                    round(float(np.percentile(t_part, 90)), 4)],
                        "lse_merge": round(float(np.mean(t_merge)), 4)},
+        "cold_cache": {"note": "1 GiB fill before each step (outside the events)",
+                       "decode_partials_median_ms": round(float(np.median(cold[:, 0])), 4),
+                       "lse_merge_median_ms": round(float(np.median(cold[:, 1])), 4),
+                       "decode_frac": round(launch_bytes / (float(np.median(cold[:, 0])) * 1e-3) / 1e9
+                                            / PEAK_HBM_GBS, 4)},
+        "single_shard": {"note": "mla_decode_partial for shard 0 of the same cache (one rank's call)",
+                         "median_ms": round(float(np.median(t_one)), 4),
+                         "algorithmic_bytes": int(one_bytes), "kv_tokens": one_tokens,
+                         "achieved_gbs": round(one_bytes / (float(np.median(t_one)) * 1e-3) / 1e9, 2),
+                         "frac": round(one_bytes / (float(np.median(t_one)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic_for(sp.name, khash),

@@ -85,7 +85,7 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
         if ((st = launch_status()) != MLA_OK) return st;
     }
     if (plan.planned) {
-        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p, plan.target,
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p, plan.target, plan.chunk_min,
                            reinterpret_cast<int32_t*>(w), reinterpret_cast<int32_t*>(w + plan.items_off),
                            reinterpret_cast<int32_t*>(w + plan.row_info_off));
         if ((st = launch_status()) != MLA_OK) return st;
@@ -125,7 +125,7 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     }
     if ((st = launch_status()) != MLA_OK) return st;
     if (plan.planned) {
-        hipLaunchKernelGGL(chunk_combine_kernel, dim3(uint32_t(plan.rows), uint32_t(d->num_heads / 4)),
+        hipLaunchKernelGGL(chunk_combine_kernel, dim3(uint32_t(plan.rows), uint32_t(d->num_heads)),
                            dim3(256), 0, s, p);
         if ((st = launch_status()) != MLA_OK) return st;
     }

@@ -65,8 +65,13 @@ int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan, int
     p.n_q = n_q;
     p.rows = int32_t(int64_t(shard_count) * n_q);
     // a row holds at most max_blocks * 64 local tokens; when that fits in one
-    // chunk of the smallest size, every row is one item and no plan is needed
-    p.planned = d->topk == 0 && int64_t(d->max_blocks) * kBlock > kChunkMin;
+    // chunk of the smallest size, every row is one item and no plan is needed.
+    // plan_target is about two items per workgroup the chip holds at once; a
+    // call with fewer rows than that many workgroups aims for one item per
+    // workgroup, with the smaller floor.
+    const bool few_rows = p.rows < plan_target(d) / 2;
+    p.chunk_min = few_rows ? kChunkSmall : kChunkMin;
+    p.planned = d->topk == 0 && int64_t(d->max_blocks) * kBlock > p.chunk_min;
     p.items_max = p.rows;
     int64_t off = kWsHeader;
     // per query token (request, index in it, its query count, 0), filled for
@@ -74,14 +79,14 @@ int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan, int
     p.qmap_off = off;
     off = align_up(off + int64_t(n_q) * 16, 256);
     if (p.planned) {
-        p.target = plan_target(d);
+        p.target = few_rows ? plan_target(d) / 2 : plan_target(d);
         // items per row <= local / chunk + 1 and sum(local) / chunk <= target
         p.items_max = p.rows + p.target;
-        // a row splits only when local > chunk >= kChunkMin, into at most
-        // 2 local / chunk items: at most 2 target and 2 total / kChunkMin
+        // a row splits only when local > chunk >= chunk_min, into at most
+        // 2 local / chunk items: at most 2 target and 2 total / chunk_min
         const int64_t total_bound = int64_t(p.rows) * d->max_blocks * kBlock;
         int64_t slots = 2 * int64_t(p.target);
-        const int64_t by_len = 2 * ((total_bound + kChunkMin - 1) / kChunkMin);
+        const int64_t by_len = 2 * ((total_bound + p.chunk_min - 1) / p.chunk_min);
         if (by_len < slots) slots = by_len;
         if (p.items_max < slots) slots = p.items_max;
         p.slots = int32_t(slots);

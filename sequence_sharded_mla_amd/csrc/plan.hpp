@@ -5,7 +5,7 @@
 // request, query token) row.  Dense steps whose rows may exceed one chunk
 // are planned on the device: a plan kernel reads the real context lengths,
 // picks a chunk size from the total work (about two chunks per resident
-// workgroup, never fewer than kChunkMin tokens), and lists (row, chunk)
+// workgroup, never fewer than the plan's floor), and lists (row, chunk)
 // items; rows of one chunk write their result directly, split rows write
 // partials into the workspace and a combine pass merges them with the same
 // LSE rule as the cross-shard merge.
@@ -24,13 +24,20 @@ constexpr int kBlock = 64;
 constexpr int kFp8Group = 128;
 constexpr int64_t kWsHeader = 256;  // int32 [0] device error word, [1] item count, [2] chunk tokens
 
-constexpr int32_t kChunkMin = 4096;  // fewest local tokens per chunk of a split row
+// Fewest local tokens per chunk of a split row.  A call with at least as
+// many rows as the chip holds workgroups splits only long rows (kChunkMin);
+// one with fewer rows (one DCP rank's share of a small batch) aims for one
+// chunk per resident workgroup, down to kChunkSmall tokens, so that every
+// compute unit gets work, at the cost of more partials for the combine.
+constexpr int32_t kChunkMin = 4096;
+constexpr int32_t kChunkSmall = 512;
 
 struct Plan {
     int32_t n_q = 0;            // query tokens per shard (B * Tq, or the varlen count)
     int32_t rows = 0;           // shard_count * n_q
     bool planned = false;       // dense rows that may split: device plan + combine
     int32_t target = 0;         // items the device plan aims for
+    int32_t chunk_min = 0;      // the device plan's floor on the chunk size
     int32_t items_max = 0;      // workgroups to launch (an upper bound on items)
     int32_t slots = 0;          // partial slots of split rows
     int64_t ws_bytes = kWsHeader; // workspace the call needs

@@ -139,24 +139,97 @@ __device__ __forceinline__ void merge_wave(int n, const T* o, size_t part_stride
     if (lse_out && lane == 0) lse_out[0] = (M == -INFINITY) ? -INFINITY : M + logf(W);
 }
 
-// Partials of split rows -> that shard's O_partial / LSE.  grid = (rows,
-// H / 4), 256 threads = 4 heads; rows of one item were written directly.
+// Weighted sum of parts j0 .. j1 - 1 of one row (weights exp(lse - M)), in
+// part order, into acc / W: lane i holds dims 8 i .. 8 i + 7; eight parts'
+// loads are in flight together.
+template <typename T>
+__device__ __forceinline__ void accumulate_parts(const T* base, size_t part_stride, const float* lse,
+                                                 size_t lse_stride, int j0, int j1, float M,
+                                                 float (&acc)[8], float& W, int lane) {
+    constexpr int kBatch = 8;
+    for (int s0 = j0; s0 < j1; s0 += 64) {
+        const float ls = s0 + lane < j1 ? lse[size_t(s0 + lane) * lse_stride] : -INFINITY;
+        const float w = (ls == -INFINITY) ? 0.f : expf(ls - M);
+        W += w;
+        const int cnt = min(64, j1 - s0);
+        for (int k0 = 0; k0 < cnt; k0 += kBatch) {
+            float v[kBatch][8];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                if (k0 + k < cnt) load8<T>(base + size_t(s0 + k0 + k) * part_stride, v[k]);
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                if (k0 + k >= cnt) break;
+                const float ws = __shfl(w, k0 + k);
+                if (ws != 0.f) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] = fmaf(ws, v[k][e], acc[e]);
+                }
+            }
+        }
+    }
+}
+
+// Partials of split rows -> that shard's O_partial / LSE.  grid = (rows, H),
+// 256 threads, one head per workgroup; rows of one item were written
+// directly.  A row of at most 64 parts is merged by one wave.  A longer row
+// (a few very long rows split into many chunks) has its parts dealt to the
+// four waves in contiguous quarters; the waves' sums meet in LDS and are
+// added in wave order, so the result is reproducible bit for bit.
+template <typename T>
+__device__ __forceinline__ void combine_head(const DecodeParams& p, int row, int h, int32_t slot0,
+                                             int32_t k) {
+    __shared__ float part_acc[4][64][8];
+    __shared__ float part_w[4];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const size_t head = size_t(row) * p.H + h;
+    const size_t s0 = size_t(slot0) * p.H + h;
+    const T* o = static_cast<const T*>(p.ws_o) + s0 * kLatent;
+    const float* lse = p.ws_lse + s0;
+    const size_t stride = size_t(p.H);
+    if (k <= 64) {
+        if (wave == 0)
+            merge_wave<T>(k, o, stride * kLatent, lse, stride, p.o_out, p.out_dtype, head * kLatent,
+                          p.lse_out + head, lane);
+        return;
+    }
+    float M = -INFINITY;  // every wave finds the same maximum
+    for (int j = lane; j < k; j += 64) M = fmaxf(M, lse[size_t(j) * stride]);
+    M = wave_max(M);
+    const int per = (k + 3) / 4;
+    const int j0 = min(k, wave * per), j1 = min(k, j0 + per);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    if (M != -INFINITY) accumulate_parts<T>(o + lane * 8, stride * kLatent, lse, stride, j0, j1, M, acc, W, lane);
+    W = wave_sum(W);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part_acc[wave][lane][e] = acc[e];
+    if (lane == 0) part_w[wave] = W;
+    __syncthreads();
+    if (wave != 0) return;
+    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float Wt = 0.f;
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] += part_acc[w][lane][e];
+        Wt += part_w[w];
+    }
+    const float inv = Wt > 0.f ? 1.f / Wt : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] *= inv;
+    store8(p.o_out, p.out_dtype, head * kLatent + lane * 8, sum);
+    if (lane == 0) p.lse_out[head] = (M == -INFINITY) ? -INFINITY : M + logf(Wt);
+}
+
 __global__ void __launch_bounds__(256) chunk_combine_kernel(DecodeParams p) {
     const int row = blockIdx.x;
     const int32_t slot0 = p.row_info[2 * size_t(row)];  // a row's slots are consecutive
     const int32_t k = p.row_info[2 * size_t(row) + 1];
     if (k <= 1) return;
-    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-    const size_t head = size_t(row) * p.H + h;
-    const size_t s0 = size_t(slot0) * p.H + h;
     if (p.out_dtype == MLA_F32)
-        merge_wave<float>(k, static_cast<const float*>(p.ws_o) + s0 * kLatent, size_t(p.H) * kLatent,
-                          p.ws_lse + s0, size_t(p.H), p.o_out, p.out_dtype, head * kLatent,
-                          p.lse_out + head, threadIdx.x & 63);
+        combine_head<float>(p, row, blockIdx.y, slot0, k);
     else
-        merge_wave<uint16_t>(k, static_cast<const uint16_t*>(p.ws_o) + s0 * kLatent,
-                             size_t(p.H) * kLatent, p.ws_lse + s0, size_t(p.H), p.o_out,
-                             p.out_dtype, head * kLatent, p.lse_out + head, threadIdx.x & 63);
+        combine_head<uint16_t>(p, row, blockIdx.y, slot0, k);
 }
 
 constexpr int kPlanThreads = 256;
@@ -195,7 +268,7 @@ __device__ __forceinline__ uint64_t block_total(uint64_t x, uint64_t* wave_tot) 
 // Device plan of a dense step (one workgroup of kPlanThreads threads).
 //
 // The chunk size T comes from the real total of local tokens (about
-// `target` items, never below kChunkMin).  Row r becomes floor(local / T)
+// `target` items, never below chunk_min).  Row r becomes floor(local / T)
 // full chunks plus one remainder chunk when local is not a multiple of T
 // (a row with no token still gets one item, which writes (0, -inf)).  Items
 // are listed longest first, so the dispatcher ends on short work: all full
@@ -208,7 +281,7 @@ __device__ __forceinline__ uint64_t block_total(uint64_t x, uint64_t* wave_tot) 
 // size classes share two scans as 16-bit fields (at most kPlanThreads per
 // field); over all rows the class counts take 32-bit fields.
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(DecodeParams p, int32_t target,
-                                                            int32_t* hdr, int32_t* items,
+                                                            int32_t chunk_min, int32_t* hdr, int32_t* items,
                                                             int32_t* row_info) {
     constexpr int kBuckets = 8;
     __shared__ uint64_t wave_tot[kPlanWaves];
@@ -229,7 +302,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(DecodeParams p, int3
     tot = block_total(tot, wave_tot);
     uint64_t chunk = (tot + uint64_t(target) - 1) / uint64_t(target);
     chunk = (chunk + kBlock - 1) / kBlock * kBlock;
-    if (chunk < uint64_t(kChunkMin)) chunk = kChunkMin;
+    if (chunk < uint64_t(chunk_min)) chunk = uint64_t(chunk_min);
     if (chunk > (uint64_t(1) << 30)) chunk = uint64_t(1) << 30;
     const int32_t T = int32_t(chunk);
 

@@ -146,6 +146,45 @@ def test_single_shard_entry_matches_shards_call():
         assert torch.equal(o, step.o_partials[s]) and torch.equal(l, step.lses[s])
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("dense_bf16_32k", dict(batch=4, seed=14)),                       # 4 rows x 4096 tokens
+    ("long_fp8_1m", dict(batch=1, context=300_000, seed=15)),         # 1 row x 37500 tokens
+])
+def test_single_shard_call_splits_rows_to_fill_the_chip(name, kw):
+    """One rank's call with fewer rows than the chip holds workgroups: the
+    plan splits rows down to 512-token chunks, and the shard's partials still
+    match the oracle's."""
+    from oracle import decode as odecode
+    from sequence_sharded_mla_amd import alloc_workspace
+    from gpu_cases import max_err, oracle_for
+    sp = S[name].with_(**kw)
+    say(f"single-shard {sp.name} {kw}")
+    x = workload.generate(sp)
+    cache = layout.pack(x, device="cuda")
+    d = cache.desc
+    ws = alloc_workspace(d, 1)
+    s = 3
+    rows = sp.batch * sp.q_len
+    dt = torch.bfloat16 if sp.out_dtype == "bf16" else torch.float32
+    o = torch.empty((rows, sp.heads, 512), dtype=dt, device="cuda")
+    l = torch.empty((rows, sp.heads), dtype=torch.float32, device="cuda")
+    mla_decode_partial(d, cache.q, cache.pool, cache.block_tables[s].contiguous(), cache.context_lens,
+                       None, s, sp.n_shards, o, l, ws)
+    torch.cuda.synchronize()
+    hdr = ws[:256].cpu().numpy().view(np.int32)
+    say(f"  items {hdr[1]} chunk {hdr[2]}")
+    assert hdr[2] < 4096 and hdr[1] > rows       # split below the large-call floor
+    assert mla_get_device_error(ws) == 0
+    ref = odecode.mla_decode(odecode.query_to_f64(x.q, sp.q_dtype),
+                             odecode.storage_rows(sp.kv_dtype, x.latent, x.scales, x.rope,
+                                                  x.row_offsets, x.row_pos),
+                             x.context_lens, sp.q_len, sp.n_shards, sp.scale, shards=[s], full=False)
+    eo = max_err(to_np(o).reshape(sp.batch, sp.q_len, sp.heads, 512), ref["o_shards"][0])
+    el = max_err(to_np(l).reshape(sp.batch, sp.q_len, sp.heads), ref["lse_shards"][0])
+    say(f"  o={eo:.3e} lse={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
 def test_bitwise_reproducible():
     sp = S["dense_fp8_mixed"].with_(batch=4, ctx_range=(1000, 9000), seed=13)
     x = workload.generate(sp)

@@ -2,8 +2,11 @@
 
 White-box: the workspace layout (256-B header, query map, items, row_info) is the
 library's own.  For each row (shard, request, query token) the plan must
-list its chunks exactly once, with the chunk size the total work gives, a
-consecutive block of partial slots for each split row, and the items
+list its chunks exactly once, with the chunk size the total work gives (about
+two items per resident workgroup, never below 4096 tokens; one item per
+resident workgroup and never below 512 for a call with fewer rows than the
+chip holds workgroups), a consecutive block of partial slots for each split
+row, and the items
 ordered longest first (all full chunks, then the remainders by size class).
 The outputs of the same steps are checked against the oracle by the parity
 tests; this checks the work split itself.
@@ -22,7 +25,8 @@ from gpu_cases import say
 
 pytestmark = pytest.mark.gpu
 
-CHUNK_MIN = 4096
+CHUNK_MIN = 4096      # chunk floor of a call that fills the chip with rows
+CHUNK_SMALL = 512     # floor of a call with fewer rows than resident workgroups
 BUCKETS = 8
 
 
@@ -56,15 +60,19 @@ def test_plan_lists_every_chunk_once_longest_first(name, kw):
     N, B, Tq = sp.n_shards, sp.batch, sp.q_len
     rows = N * B * Tq
     cap = cache.max_blocks * 64
-    assert cap > CHUNK_MIN, "this case must be planned"
+    target = target_for(sp)
+    few_rows = rows < target // 2
+    floor = CHUNK_SMALL if few_rows else CHUNK_MIN
+    if few_rows:
+        target //= 2          # one item per resident workgroup
+    assert cap > floor, "this case must be planned"
     local = np.zeros(rows, np.int64)
     for r in range(rows):
         t, bt = r % Tq, r // Tq
         b, s = bt % B, bt // B
         visible = max(int(x.context_lens[b]) - Tq + t + 1, 0)
         local[r] = min(int(sharding.local_len(visible, s, N)), cap)
-    target = target_for(sp)
-    T = max(CHUNK_MIN, -(-(-(-int(local.sum()) // target)) // 64) * 64)
+    T = max(floor, -(-(-(-int(local.sum()) // target)) // 64) * 64)
     hdr = ws[:256].view(np.int32)
     assert hdr[2] == T
     full = local // T
