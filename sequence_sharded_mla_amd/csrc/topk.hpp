@@ -70,8 +70,8 @@ struct MergeParams {
 // -0 and +0 map to the same value.
 __device__ __forceinline__ uint32_t score_bits(float x) {
     uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) == 0) u = 0;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    u = (u << 1) == 0 ? 0u : u;                              // -0 -> +0
+    return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);  // negative: ~u; else set the sign
 }
 
 __device__ __forceinline__ uint64_t make_key(float score, uint32_t id) {
@@ -470,49 +470,54 @@ __device__ bool select_one_pass(SelectShared& sh, SelList& buf, const Src& src, 
             }
             __syncthreads();
         }
-        // digit of element (u, v), or 0 when it is past the row
-        auto digit = [&](int u, int v) -> uint32_t {
-            const int32_t i = (g0 + u * kThreads) * V + v;
-            return i < n32 ? score_bits(x[u][v]) >> 20 : 0u;
+        // Only elements whose digit is at least D are counted and kept: the
+        // K-th key's digit is found among them or the row takes the general
+        // path.  A batch wholly inside the row skips the per-element test
+        // against the row's end.
+        auto run = [&](auto check_c) {
+            constexpr bool CHECK = decltype(check_c)::value;
+            auto keep = [&](int u, int v, uint32_t b) {
+                return (!CHECK || (g0 + u * kThreads) * V + v < n32) && (b >> 20) >= d_min;
+            };
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const uint32_t b = score_bits(x[u][v]);
+                    if (keep(u, v, b)) {
+                        atomicAdd(&sh.hist[b >> 20], 1u);
+                        ++cnt;
+                    }
+                }
+            uint32_t incl = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            const uint32_t tot = __shfl(incl, 63);
+            if (tot == 0) return;
+            uint32_t at = 0;
+            if (lane == 0) at = atomicAdd(&buf.n, tot);
+            at = __shfl(at, 0) + incl - cnt;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const uint32_t b = score_bits(x[u][v]);
+                    if (!keep(u, v, b)) continue;
+                    if (at < uint32_t(kBuf)) {
+                        buf.sb[at] = b;
+                        buf.idx[at] = uint32_t((g0 + u * kThreads) * V + v);
+                    }
+                    ++at;
+                }
         };
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int v = 0; v < V; ++v) {
-                const uint32_t d = digit(u, v);
-                // only digits >= D are counted: the K-th key's digit is found
-                // among them or the row takes the general path (d_min >= 1
-                // whenever past-the-row elements could pass)
-                if (d >= d_min && (d_min > 0 || (g0 + u * kThreads) * V + v < n32)) {
-                    atomicAdd(&sh.hist[d], 1u);
-                    ++cnt;
-                }
-            }
-        uint32_t incl = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
-        const uint32_t tot = __shfl(incl, 63);
-        if (tot == 0) continue;
-        uint32_t at = 0;
-        if (lane == 0) at = atomicAdd(&buf.n, tot);
-        at = __shfl(at, 0) + incl - cnt;
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int v = 0; v < V; ++v) {
-                const int32_t i = (g0 + u * kThreads) * V + v;
-                const uint32_t d = digit(u, v);
-                if (!(d >= d_min && (d_min > 0 || i < n32))) continue;
-                if (at < uint32_t(kBuf)) {
-                    buf.sb[at] = score_bits(x[u][v]);
-                    buf.idx[at] = uint32_t(i);
-                }
-                ++at;
-            }
+        if ((base + kThreads * U) * V <= n32)
+            run(std::false_type{});
+        else
+            run(std::true_type{});
     }
     __syncthreads();
     pick_digit(sh, sh.hist, kBins, 52);
