@@ -95,6 +95,28 @@ def shard_bytes(x, s, out_bytes=2, q_bytes=2):
         B * Tq * H * (512 * out_bytes + 4), tokens
 
 
+def copy_rate_gbs(reps=5):
+    """Bytes moved (read + write) per second by a plain 1 GiB device copy,
+    the median of `reps` copies: a practical HBM reference measured in the
+    same run (a copy reaches less than a pure read stream)."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b
+    return 2 * n / (float(np.median(ts)) * 1e-3) / 1e9
+
+
 def cpu_baseline(x, budget_s=10.0):
     """Time the float64 oracle (shard partials + merge) on whole requests."""
     from threadpoolctl import threadpool_info
@@ -547,6 +569,10 @@ def main():
                      "algorithmic_bytes_per_launch": int(launch_bytes)},
         "kernel_hash": khash,
     }
+    copy_gbs = copy_rate_gbs()
+    rec["hbm_reference"] = {"copy_gbs": round(copy_gbs, 1),
+                            "note": "1 GiB device copy in the same run, read + write bytes",
+                            "decode_frac_of_copy": round(achieved / copy_gbs, 4)}
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host")
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)

@@ -781,15 +781,21 @@ __global__ void __launch_bounds__(kThreads) merge_topk_staged_kernel(MergeParams
     } else {
         select_into_bitmap<8, false>(sh, src, n, uint32_t(p.K), bits);
     }
-    // the chosen positions, sorted ascending in the tied-group space
+    // The chosen positions, compacted in candidate order (the tied-group
+    // space holds two lists of kCand); wpre[w] = chosen before word w.
     int32_t* chosen = reinterpret_cast<int32_t*>(sh.cand_key);
+    int32_t* merged = chosen + kCand;
+    __shared__ uint32_t wpre[kN / 32];
+    __shared__ uint32_t unsorted;
     const int per = (words + kThreads - 1) / kThreads;
     const int w0 = threadIdx.x * per;
     uint32_t cnt = 0;
     for (int w = w0; w < w0 + per && w < words; ++w) cnt += __popc(bits[w]);
     uint32_t total;
     uint32_t pos = block_excl_scan_u32(cnt, sh.scan, total);
+    if (threadIdx.x == 0) unsorted = 0;
     for (int w = w0; w < w0 + per && w < words; ++w) {
+        wpre[w] = pos;
         uint32_t m = bits[w];
         while (m) {
             const int bit = __builtin_ctz(m);
@@ -797,27 +803,82 @@ __global__ void __launch_bounds__(kThreads) merge_topk_staged_kernel(MergeParams
             chosen[pos++] = idx_s[w * 32 + bit];
         }
     }
-    uint32_t pw = 1;
-    while (pw < total) pw <<= 1;
-    for (uint32_t i = total + threadIdx.x; i < pw; i += kThreads) chosen[i] = INT32_MAX;
     __syncthreads();
-    for (uint32_t size = 2; size <= pw; size <<= 1) {
-        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-            for (uint32_t i = threadIdx.x; i < pw / 2; i += kThreads) {
-                const uint32_t lo = 2 * i - (i & (stride - 1));
-                const uint32_t hi = lo + stride;
-                const bool asc = (lo & size) == 0;
-                const int32_t a = chosen[lo], c = chosen[hi];
-                if ((a > c) == asc) {
-                    chosen[lo] = c;
-                    chosen[hi] = a;
+    // chosen entries of list l start at run(l); a list of mla_topk_local is
+    // ascending, so its chosen entries form a sorted run
+    auto run = [&](int l) -> uint32_t {
+        if (l >= p.n_lists) return total;
+        const uint32_t c = uint32_t(l) * uint32_t(p.k_in);
+        const uint32_t w = c >> 5, b = c & 31u;
+        return w >= uint32_t(words) ? total : wpre[w] + __popc(bits[w] & ((1u << b) - 1u));
+    };
+    auto run_of = [&](uint32_t c) {  // list whose run holds compacted entry c
+        int lo = 0, hi = p.n_lists - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (run(mid) <= c) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    };
+    const bool tree = p.n_lists <= 64;
+    if (tree) {
+        for (uint32_t c = threadIdx.x; c < total; c += kThreads)
+            if (c > run(run_of(c)) && chosen[c - 1] > chosen[c]) unsorted = 1;
+        __syncthreads();
+    }
+    const int32_t* result = chosen;
+    if (tree && !unsorted) {
+        // Pairwise merges of sorted runs, log2(n_lists) levels: an entry's
+        // place in the merged run is its index in its own run plus the
+        // entries of the partner run below it (positions are distinct).
+        int32_t* src_b = chosen;
+        int32_t* dst_b = merged;
+        for (int span = 1; span < p.n_lists; span <<= 1) {
+            for (uint32_t c = threadIdx.x; c < total; c += kThreads) {
+                const int l = run_of(c) / span;  // run index at this level
+                const int mate = l ^ 1;
+                const uint32_t a0 = run(l * span);
+                const uint32_t b0 = run(mate * span), b1 = run((mate + 1) * span);
+                const int32_t v = src_b[c];
+                uint32_t lo = b0, hi = b1;  // first partner entry >= v
+                while (lo < hi) {
+                    const uint32_t mid = (lo + hi) >> 1;
+                    if (src_b[mid] < v) lo = mid + 1;
+                    else hi = mid;
                 }
+                dst_b[run((l & ~1) * span) + (c - a0) + (lo - b0)] = v;
             }
             __syncthreads();
+            int32_t* t = src_b;
+            src_b = dst_b;
+            dst_b = t;
+        }
+        result = src_b;
+    } else {
+        // candidate lists in no particular order: bitonic sort in LDS
+        uint32_t pw = 1;
+        while (pw < total) pw <<= 1;
+        for (uint32_t i = total + threadIdx.x; i < pw; i += kThreads) chosen[i] = INT32_MAX;
+        __syncthreads();
+        for (uint32_t size = 2; size <= pw; size <<= 1) {
+            for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+                for (uint32_t i = threadIdx.x; i < pw / 2; i += kThreads) {
+                    const uint32_t lo = 2 * i - (i & (stride - 1));
+                    const uint32_t hi = lo + stride;
+                    const bool asc = (lo & size) == 0;
+                    const int32_t a = chosen[lo], c = chosen[hi];
+                    if ((a > c) == asc) {
+                        chosen[lo] = c;
+                        chosen[hi] = a;
+                    }
+                }
+                __syncthreads();
+            }
         }
     }
     int32_t* out = p.out_idx + size_t(row) * p.K;
-    for (int32_t i = threadIdx.x; i < p.K; i += kThreads) out[i] = uint32_t(i) < total ? chosen[i] : -1;
+    for (int32_t i = threadIdx.x; i < p.K; i += kThreads) out[i] = uint32_t(i) < total ? result[i] : -1;
 }
 
 }  // namespace topk

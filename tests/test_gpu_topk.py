@@ -137,3 +137,28 @@ def test_full_size_selection_sampled():
         s = int(rng.integers(N))
         ref_p, _ = otk.local_topk(scores[b:b + 1], lens[b:b + 1], Tq, K, s, N)
         assert np.array_equal(ci_h[s, b], ref_p[0])
+
+
+def test_merge_of_lists_in_any_order():
+    """mla_topk_merge takes candidate lists in any order: the shards' lists
+    shuffled within each row give the same selection (the ascending lists of
+    mla_topk_local take the merge of sorted runs, these the general sort)."""
+    B, Tq, L, K, N = 3, 2, 30000, 2048, 8
+    lens = np.array([L, 20000, 9000])
+    scores = workload.indexer_scores(B, Tq, L, seed=600)
+    sc_sh = layout.shard_scores(scores, N)
+    ci, cs = run_local(sc_sh, lens, K, 0, N)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(601)
+    ci_h = ci.cpu().numpy().reshape(N, B * Tq, K)
+    cs_h = cs.cpu().numpy().reshape(N, B * Tq, K)
+    for s in range(N):
+        for r in range(B * Tq):
+            perm = rng.permutation(K)
+            ci_h[s, r] = ci_h[s, r, perm]
+            cs_h[s, r] = cs_h[s, r, perm]
+    merged = torch.empty((B * Tq, K), dtype=torch.int32, device="cuda")
+    mla_topk_merge(torch.from_numpy(ci_h).cuda(), torch.from_numpy(cs_h).cuda(), K, merged)
+    torch.cuda.synchronize()
+    ref = otk.global_topk(scores, lens, Tq, K)
+    assert np.array_equal(merged.cpu().numpy().reshape(B, Tq, K), ref)
