@@ -411,7 +411,9 @@ def main():
     ap.add_argument("--topk", action="store_true",
                     help="time the top-K index selection (per-shard local top-K + merge)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="with --kv-write: time only the fused all-shard call (for profiling)")
+                    help="time only the timed region's launches (for profiling): with --kv-write the "
+                         "fused all-shard call; for the decode step no cold-cache, single-shard or "
+                         "copy series")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     args = ap.parse_args()
@@ -478,12 +480,13 @@ def main():
     t_merge = np.array([e[1].elapsed_time(e[2]) for e in ev])
     assert mla_get_device_error(step.workspace) == 0
 
+    extras = not args.no_extras
     # Cold-cache series (not the timed region): a 1 GiB fill before every
     # step evicts the 256 MB last-level cache, so no KV row of the previous
     # step is served from it; only the events around the launches count.
-    evict = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    evict = torch.empty(1 << 30 if extras else 1, dtype=torch.uint8, device="cuda")
     cold = []
-    for i in range(K):
+    for i in range(K if extras else 0):
         evict.fill_(i & 0xff)
         a, b, c = ev[i]
         a.record(stream)
@@ -493,7 +496,7 @@ def main():
         c.record(stream)
         torch.cuda.synchronize()
         cold.append((a.elapsed_time(b), b.elapsed_time(c)))
-    cold = np.array(cold)
+    cold = np.array(cold).reshape(-1, 2)
     del evict
     assert mla_get_device_error(step.workspace) == 0
 
@@ -510,17 +513,17 @@ def main():
     def one_shard():
         mla_decode_partial(d, cache.q, cache.pool, bt0, cache.context_lens, cache.topk_idx, 0,
                            cache.n_shards, o1, l1, ws1)
-    for _ in range(3):
+    for _ in range(3 if extras else 0):
         one_shard()
     torch.cuda.synchronize()
     t_one = []
-    for i in range(K):
+    for i in range(K if extras else 0):
         a, b, _ = ev[i]
         a.record(stream)
         one_shard()
         b.record(stream)
     torch.cuda.synchronize()
-    t_one = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    t_one = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K if extras else 0)])
     assert mla_get_device_error(ws1) == 0
     one_bytes, one_tokens = shard_bytes(x, 0, out_b, q_b)
 
@@ -552,16 +555,18 @@ def main():
                        "decode_partials_p10_p90": [round(float(np.percentile(t_part, 10)), 4),
                                                    round(float(np.percentile(t_part, 90)), 4)],
                        "lse_merge": round(float(np.mean(t_merge)), 4)},
-        "cold_cache": {"note": "1 GiB fill before each step (outside the events)",
-                       "decode_partials_median_ms": round(float(np.median(cold[:, 0])), 4),
-                       "lse_merge_median_ms": round(float(np.median(cold[:, 1])), 4),
-                       "decode_frac": round(launch_bytes / (float(np.median(cold[:, 0])) * 1e-3) / 1e9
-                                            / PEAK_HBM_GBS, 4)},
-        "single_shard": {"note": "mla_decode_partial for shard 0 of the same cache (one rank's call)",
-                         "median_ms": round(float(np.median(t_one)), 4),
-                         "algorithmic_bytes": int(one_bytes), "kv_tokens": one_tokens,
-                         "achieved_gbs": round(one_bytes / (float(np.median(t_one)) * 1e-3) / 1e9, 2),
-                         "frac": round(one_bytes / (float(np.median(t_one)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "cold_cache": None if not extras else {
+            "note": "1 GiB fill before each step (outside the events)",
+            "decode_partials_median_ms": round(float(np.median(cold[:, 0])), 4),
+            "lse_merge_median_ms": round(float(np.median(cold[:, 1])), 4),
+            "decode_frac": round(launch_bytes / (float(np.median(cold[:, 0])) * 1e-3) / 1e9
+                                 / PEAK_HBM_GBS, 4)},
+        "single_shard": None if not extras else {
+            "note": "mla_decode_partial for shard 0 of the same cache (one rank's call)",
+            "median_ms": round(float(np.median(t_one)), 4),
+            "algorithmic_bytes": int(one_bytes), "kv_tokens": one_tokens,
+            "achieved_gbs": round(one_bytes / (float(np.median(t_one)) * 1e-3) / 1e9, 2),
+            "frac": round(one_bytes / (float(np.median(t_one)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic_for(sp.name, khash),
@@ -569,10 +574,11 @@ def main():
                      "algorithmic_bytes_per_launch": int(launch_bytes)},
         "kernel_hash": khash,
     }
-    copy_gbs = copy_rate_gbs()
-    rec["hbm_reference"] = {"copy_gbs": round(copy_gbs, 1),
-                            "note": "1 GiB device copy in the same run, read + write bytes",
-                            "decode_frac_of_copy": round(achieved / copy_gbs, 4)}
+    if extras:
+        copy_gbs = copy_rate_gbs()
+        rec["hbm_reference"] = {"copy_gbs": round(copy_gbs, 1),
+                                "note": "1 GiB device copy in the same run, read + write bytes",
+                                "decode_frac_of_copy": round(achieved / copy_gbs, 4)}
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host")
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
