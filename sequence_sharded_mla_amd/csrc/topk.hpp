@@ -140,6 +140,12 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t x, uint32_t* wa
     return before + inc - x;
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = max(x, uint32_t(__shfl_xor(int(x), o)));
+    return x;
+}
+
 // Finds the digit holding the need-th largest key among the histogram's
 // bins (nbins <= kBins), updates prefix/mask/need/tied.  All threads call.
 __device__ __forceinline__ void pick_digit(SelectShared& sh, const uint32_t* hist, int nbins, int shift) {
@@ -804,27 +810,92 @@ __global__ void __launch_bounds__(kThreads) merge_topk_staged_kernel(MergeParams
         }
     }
     __syncthreads();
-    // chosen entries of list l start at run(l); a list of mla_topk_local is
-    // ascending, so its chosen entries form a sorted run
-    auto run = [&](int l) -> uint32_t {
-        if (l >= p.n_lists) return total;
-        const uint32_t c = uint32_t(l) * uint32_t(p.k_in);
-        const uint32_t w = c >> 5, b = c & 31u;
-        return w >= uint32_t(words) ? total : wpre[w] + __popc(bits[w] & ((1u << b) - 1u));
-    };
-    auto run_of = [&](uint32_t c) {  // list whose run holds compacted entry c
-        int lo = 0, hi = p.n_lists - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (run(mid) <= c) lo = mid;
-            else hi = mid - 1;
+    // Ascending order.  When every chosen position is below 2^19, the
+    // staging arrays (free now) hold a bitmap over positions: an entry's
+    // output index is the number of set bits before its own.  Otherwise the
+    // lists' sorted runs are merged, or sorted when a list is not ascending.
+    constexpr int kPerT = kCand / kThreads;
+    constexpr uint32_t kPosBits = uint32_t(kN) * 32;  // idx_s as a bitmap
+    __shared__ uint32_t max_pos;
+    if (threadIdx.x == 0) max_pos = 0;
+    __syncthreads();
+    {
+        uint32_t mx = 0;
+#pragma unroll
+        for (int k = 0; k < kPerT; ++k) {
+            const uint32_t c = threadIdx.x + k * kThreads;
+            if (c < total) mx = max(mx, uint32_t(chosen[c]));
         }
-        return lo;
-    };
+        mx = uint32_t(wave_max_u32(mx));
+        if ((threadIdx.x & 63) == 0) atomicMax(&max_pos, mx);
+    }
+    __syncthreads();
+    if (total > 0 && max_pos < kPosBits) {
+        uint32_t* pbits = reinterpret_cast<uint32_t*>(idx_s);
+        uint32_t* pre = reinterpret_cast<uint32_t*>(sc_s);  // set bits before each word
+        const uint32_t nw = max_pos / 32 + 1;
+        for (uint32_t w = threadIdx.x; w < nw; w += kThreads) pbits[w] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kPerT; ++k) {
+            const uint32_t c = threadIdx.x + k * kThreads;
+            if (c < total) atomicOr(&pbits[uint32_t(chosen[c]) >> 5], 1u << (uint32_t(chosen[c]) & 31u));
+        }
+        __syncthreads();
+        const uint32_t per_w = (nw + kThreads - 1) / kThreads;
+        const uint32_t wb = threadIdx.x * per_w;
+        uint32_t mine = 0;
+        for (uint32_t w = wb; w < wb + per_w && w < nw; ++w) mine += __popc(pbits[w]);
+        uint32_t all;
+        uint32_t run_b = block_excl_scan_u32(mine, sh.scan, all);
+        for (uint32_t w = wb; w < wb + per_w && w < nw; ++w) {
+            pre[w] = run_b;
+            run_b += __popc(pbits[w]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kPerT; ++k) {
+            const uint32_t c = threadIdx.x + k * kThreads;
+            if (c >= total) continue;
+            const uint32_t v = uint32_t(chosen[c]);
+            merged[pre[v >> 5] + __popc(pbits[v >> 5] & ((1u << (v & 31u)) - 1u))] = int32_t(v);
+        }
+        __syncthreads();
+        int32_t* out = p.out_idx + size_t(row) * p.K;
+        for (int32_t i = threadIdx.x; i < p.K; i += kThreads) out[i] = uint32_t(i) < total ? merged[i] : -1;
+        return;
+    }
+    // chosen entries of list l start at rs[l] (rs[n_lists] = total); a list
+    // of mla_topk_local is ascending, so its chosen entries form a sorted run
     const bool tree = p.n_lists <= 64;
+    __shared__ uint32_t rs[65];
+    if (tree && int(threadIdx.x) <= p.n_lists) {
+        const uint32_t c = uint32_t(threadIdx.x) * uint32_t(p.k_in);
+        const uint32_t w = c >> 5, b = c & 31u;
+        rs[threadIdx.x] = (int(threadIdx.x) == p.n_lists || w >= uint32_t(words))
+                              ? total : wpre[w] + __popc(bits[w] & ((1u << b) - 1u));
+    }
+    __syncthreads();
+    // a thread's entries c = tid + k * kThreads; their searches advance in
+    // step, so the LDS reads of one step are in flight together
+    int lrun[kPerT];  // list (run) of each entry
+#pragma unroll
+    for (int k = 0; k < kPerT; ++k) lrun[k] = 0;
     if (tree) {
-        for (uint32_t c = threadIdx.x; c < total; c += kThreads)
-            if (c > run(run_of(c)) && chosen[c - 1] > chosen[c]) unsorted = 1;
+        for (int step = 32; step > 0; step >>= 1) {
+#pragma unroll
+            for (int k = 0; k < kPerT; ++k) {
+                const uint32_t c = threadIdx.x + k * kThreads;
+                const int t = lrun[k] + step;
+                const uint32_t r = rs[t < p.n_lists ? t : p.n_lists];  // rs[n_lists] = total
+                lrun[k] = (t < p.n_lists && r <= c) ? t : lrun[k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kPerT; ++k) {
+            const uint32_t c = threadIdx.x + k * kThreads;
+            if (c < total && c > rs[lrun[k]] && chosen[c - 1] > chosen[c]) unsorted = 1;
+        }
         __syncthreads();
     }
     const int32_t* result = chosen;
@@ -834,20 +905,40 @@ __global__ void __launch_bounds__(kThreads) merge_topk_staged_kernel(MergeParams
         // entries of the partner run below it (positions are distinct).
         int32_t* src_b = chosen;
         int32_t* dst_b = merged;
-        for (int span = 1; span < p.n_lists; span <<= 1) {
-            for (uint32_t c = threadIdx.x; c < total; c += kThreads) {
-                const int l = run_of(c) / span;  // run index at this level
-                const int mate = l ^ 1;
-                const uint32_t a0 = run(l * span);
-                const uint32_t b0 = run(mate * span), b1 = run((mate + 1) * span);
-                const int32_t v = src_b[c];
-                uint32_t lo = b0, hi = b1;  // first partner entry >= v
-                while (lo < hi) {
-                    const uint32_t mid = (lo + hi) >> 1;
-                    if (src_b[mid] < v) lo = mid + 1;
-                    else hi = mid;
+        const int nl = p.n_lists;
+        auto start = [&](int l) { return rs[l < nl ? l : nl]; };
+        for (int span = 1; span < nl; span <<= 1) {
+            uint32_t lo[kPerT], len[kPerT], b0[kPerT];
+            int32_t v[kPerT];
+#pragma unroll
+            for (int k = 0; k < kPerT; ++k) {
+                const uint32_t c = threadIdx.x + k * kThreads;
+                const int l = lrun[k] / span, mate = l ^ 1;
+                b0[k] = start(mate * span);
+                lo[k] = b0[k];
+                len[k] = start((mate + 1) * span) - b0[k];
+                v[k] = src_b[c < total ? c : 0];
+            }
+            // first partner entry >= v: a fixed number of halving steps with
+            // no branch, so the four searches' reads go out together
+            const uint32_t last = total > 0 ? total - 1 : 0;
+            for (int it = 0; it < 12; ++it) {
+#pragma unroll
+                for (int k = 0; k < kPerT; ++k) {
+                    const uint32_t half = len[k] >> 1;
+                    const uint32_t probe = lo[k] + half;
+                    const int32_t x = src_b[probe < last ? probe : last];
+                    const bool go = len[k] > 0 && x < v[k];
+                    lo[k] = go ? probe + 1 : lo[k];
+                    len[k] = len[k] == 0 ? 0u : (go ? len[k] - half - 1 : half);
                 }
-                dst_b[run((l & ~1) * span) + (c - a0) + (lo - b0)] = v;
+            }
+#pragma unroll
+            for (int k = 0; k < kPerT; ++k) {
+                const uint32_t c = threadIdx.x + k * kThreads;
+                if (c >= total) continue;
+                const int l = lrun[k] / span;
+                dst_b[start((l & ~1) * span) + (c - start(l * span)) + (lo[k] - b0[k])] = v[k];
             }
             __syncthreads();
             int32_t* t = src_b;

@@ -162,3 +162,31 @@ def test_merge_of_lists_in_any_order():
     torch.cuda.synchronize()
     ref = otk.global_topk(scores, lens, Tq, K)
     assert np.array_equal(merged.cpu().numpy().reshape(B, Tq, K), ref)
+
+
+@pytest.mark.parametrize("shuffled", [False, True])
+def test_merge_with_positions_beyond_the_bitmap(shuffled):
+    """Candidate positions up to 2^30 (past the merge's position bitmap): the
+    chosen entries are ordered by merging the lists' ascending runs, or by a
+    sort when the lists are shuffled; the selection matches the oracle's."""
+    rng = np.random.default_rng(700 + shuffled)
+    n_lists, rows, k_in, K = 8, 5, 1500, 2048
+    ci = np.full((n_lists, rows, k_in), -1, dtype=np.int32)
+    cs = np.full((n_lists, rows, k_in), -np.inf, dtype=np.float32)
+    for r in range(rows):
+        pos = rng.choice(1 << 30, size=n_lists * k_in, replace=False).astype(np.int64)
+        for s in range(n_lists):
+            n_s = int(rng.integers(k_in // 2, k_in + 1))
+            p_s = np.sort(pos[s * k_in: s * k_in + n_s])
+            sc = rng.standard_normal(n_s).astype(np.float32)
+            sc[rng.random(n_s) < 0.2] = 0.5                  # ties among lists
+            if shuffled:
+                perm = rng.permutation(n_s)
+                p_s, sc = p_s[perm], sc[perm]
+            ci[s, r, :n_s] = p_s
+            cs[s, r, :n_s] = sc
+    out = torch.empty((rows, K), dtype=torch.int32, device="cuda")
+    mla_topk_merge(torch.from_numpy(ci).cuda(), torch.from_numpy(cs).cuda(), K, out)
+    torch.cuda.synchronize()
+    ref = otk.merge_topk(ci, cs, K)
+    assert np.array_equal(out.cpu().numpy(), ref)
