@@ -792,14 +792,17 @@ __global__ void __launch_bounds__(kThreads) merge_topk_staged_kernel(MergeParams
     int32_t* chosen = reinterpret_cast<int32_t*>(sh.cand_key);
     int32_t* merged = chosen + kCand;
     __shared__ uint32_t wpre[kN / 32];
-    __shared__ uint32_t unsorted;
+    __shared__ uint32_t unsorted, max_pos;
     const int per = (words + kThreads - 1) / kThreads;
     const int w0 = threadIdx.x * per;
     uint32_t cnt = 0;
     for (int w = w0; w < w0 + per && w < words; ++w) cnt += __popc(bits[w]);
     uint32_t total;
     uint32_t pos = block_excl_scan_u32(cnt, sh.scan, total);
-    if (threadIdx.x == 0) unsorted = 0;
+    if (threadIdx.x == 0) {
+        unsorted = 0;
+        max_pos = 0;
+    }
     for (int w = w0; w < w0 + per && w < words; ++w) {
         wpre[w] = pos;
         uint32_t m = bits[w];
@@ -816,9 +819,6 @@ __global__ void __launch_bounds__(kThreads) merge_topk_staged_kernel(MergeParams
     // lists' sorted runs are merged, or sorted when a list is not ascending.
     constexpr int kPerT = kCand / kThreads;
     constexpr uint32_t kPosBits = uint32_t(kN) * 32;  // idx_s as a bitmap
-    __shared__ uint32_t max_pos;
-    if (threadIdx.x == 0) max_pos = 0;
-    __syncthreads();
     {
         uint32_t mx = 0;
 #pragma unroll
