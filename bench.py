@@ -34,6 +34,8 @@ KERNEL_SOURCES = ["decode_valu.hpp", "decode_mfma.hpp", "decode_fp8.hpp", "mfma_
 WRITE_SOURCES = ["kv_write.hpp", "common.hpp", "api.hip"]
 TOPK_SOURCES = ["topk.hpp", "common.hpp", "api.hip"]
 TOPK_METRIC = "DCP top-K index selection: achieved HBM GB/s (% of peak) and rows/s, per-shard top-2048 + merge"
+VARLEN_METRIC = ("MLA varlen decode attention (1 or 2 query tokens per request): achieved HBM GB/s "
+                 "(% of peak) and KV tokens/s")
 WRITE_METRIC = "DCP KV cache write: achieved HBM GB/s (% of peak) and tokens/s, 1M tokens over 8 shards"
 
 
@@ -397,6 +399,129 @@ def run_kv_write(args):
     print(json.dumps(rec), flush=True)
 
 
+def varlen_cpu_baseline(x, q, qsl, budget_s=10.0):
+    """Time the float64 oracle's varlen step (shard partials + merge) on
+    whole requests, one request's tokens per call."""
+    from threadpoolctl import threadpool_info
+    from oracle import decode as odecode
+    sp = x.spec
+    qf = odecode.query_to_f64(q, sp.q_dtype)
+    rows = odecode.storage_rows(sp.kv_dtype, x.latent, x.scales, x.rope, x.row_offsets, x.row_pos)
+    done, tokens, t0 = 0, 0, time.perf_counter()
+    while done < sp.batch and (time.perf_counter() - t0) < budget_s:
+        b = done
+        toks = list(range(int(qsl[b]), int(qsl[b + 1])))
+        if toks:
+            odecode.mla_decode_varlen(qf, rows, x.context_lens, qsl, sp.n_shards, sp.scale,
+                                      tokens=toks)
+        c = len(toks)
+        tokens += sum(max(int(x.context_lens[b]) - c + t + 1, 0) for t in range(c))
+        done += 1
+    dt = time.perf_counter() - t0
+    from sequence_sharded_mla_amd.layout import ROW_BYTES
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(tokens * ROW_BYTES[sp.kv_dtype] / dt / 1e9, 4), "unit": "GB/s",
+            "kv_tokens_per_s": round(tokens / dt, 1), "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {sp.batch} requests ({int(qsl[done])} query tokens, all "
+                      f"{sp.n_shards} shards + merge), {tokens} attended tokens, {dt:.1f} s"}
+
+
+def run_varlen(args):
+    """Varlen decode step: requests of the fp8 mixed-length cache carry one
+    or two query tokens (multi-token-prediction drafts) in one call."""
+    import torch
+    import workload
+    from sequence_sharded_mla_amd import layout, mla_get_device_error
+    from sequence_sharded_mla_amd.layout import ROW_BYTES
+    from sequence_sharded_mla_amd.step import VarlenDecodeStep
+    name = "varlen_fp8_mtp2"
+    w = workload.VARLEN_SPECS[name]
+    sp = workload.SPECS[w["base"]].with_(q_len=w["q_len"])
+    log(f"bench: generating {name} ({sp.name} with {sp.q_len} query tokens per request)")
+    x = workload.generate(sp)
+    counts = workload.varlen_counts(sp.batch, sp.q_len, w["seed"])
+    sel = [(b, j) for b, c in enumerate(counts) for j in range(sp.q_len - int(c), sp.q_len)]
+    q = np.stack([x.q[b, j] for b, j in sel])
+    qsl = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    n_q = int(qsl[-1])
+    cache = layout.pack(x, device="cuda")
+    dq = torch.from_numpy(np.ascontiguousarray(q).view(np.int16)).cuda().view(torch.bfloat16)
+    step = VarlenDecodeStep(cache, sp.out_dtype, dq, torch.from_numpy(qsl).cuda())
+    stream = torch.cuda.current_stream()
+
+    H, N = sp.heads, sp.n_shards
+    tokens = int(sum(max(int(L) - int(c) + t + 1, 0)
+                     for L, c in zip(x.context_lens, counts) for t in range(int(c))))
+    part = N * n_q * H * (512 * 2 + 4)
+    launch_bytes = tokens * ROW_BYTES[sp.kv_dtype] + n_q * H * 576 * 2 + qsl.size * 4 + part
+    step_bytes = launch_bytes + part + n_q * H * (512 * 2 + 4)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert mla_get_device_error(step.workspace) == 0
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    log(f"bench: timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        a, b, c = ev[i]
+        a.record(stream)
+        step.partials()
+        b.record(stream)
+        step.merge()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_part = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    t_merge = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    assert mla_get_device_error(step.workspace) == 0
+    ms_step = wall * 1e3 / K
+    part_ms = float(np.mean(t_part))
+    achieved = launch_bytes / (part_ms * 1e-3) / 1e9
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    khash = kernel_hash()
+    rec = {
+        "metric": VARLEN_METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) query/latent/rope, random-permuted paged blocks, "
+                "seeded query counts)",
+        "config": {"workload": name, "batch": sp.batch, "q_len_max": sp.q_len,
+                   "query_tokens": n_q, "heads": H, "context": list(sp.ctx_range),
+                   "n_shards": N, "kv_cache": sp.kv_dtype, "block_size": 64},
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "kernels_ms": {"decode_partials": round(part_ms, 4),
+                       "decode_partials_median": round(float(np.median(t_part)), 4),
+                       "lse_merge": round(float(np.mean(t_merge)), 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for(name, khash),
+                     "kernel": "varlen decode partials (all shards, one launch)",
+                     "algorithmic_bytes_per_launch": int(launch_bytes)},
+        "kernel_hash": khash,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host")
+        rec["cpu_baseline"] = varlen_cpu_baseline(x, q, qsl, args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +535,8 @@ def main():
                          "of the decode step")
     ap.add_argument("--topk", action="store_true",
                     help="time the top-K index selection (per-shard local top-K + merge)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time the varlen decode step (1 or 2 query tokens per request)")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the timed region's launches (for profiling): with --kv-write the "
                          "fused all-shard call; for the decode step no cold-cache, single-shard or "
@@ -437,6 +564,9 @@ def main():
         return
     if args.topk:
         run_topk(args)
+        return
+    if args.varlen:
+        run_varlen(args)
         return
     import workload
     from sequence_sharded_mla_amd import layout, mla_get_device_error

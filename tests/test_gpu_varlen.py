@@ -133,3 +133,21 @@ def test_offsets_not_a_partition_raise_the_error_word():
         torch.cuda.synchronize()
         assert mla_get_device_error(step.workspace) & MLA_DEVERR_QUERY, bad
         assert torch.all(torch.isfinite(step.o.float()))
+
+
+def test_full_size_varlen_sampled():
+    """The varlen workload bench.py times (the fp8 mixed-length cache, 64
+    requests holding 1 or 2 query tokens), checked on sampled tokens: both
+    tokens of the two shortest two-token requests, the token of the shortest
+    one-token request, and the call's last token."""
+    w = workload.VARLEN_SPECS["varlen_fp8_mtp2"]
+    sp = S[w["base"]].with_(q_len=w["q_len"])
+    x = workload.generate(sp)
+    counts = workload.varlen_counts(sp.batch, sp.q_len, w["seed"])
+    qsl = np.concatenate([[0], np.cumsum(counts)])
+    by_len = np.argsort(x.context_lens, kind="stable")
+    two = [int(b) for b in by_len if counts[b] == 2][:2]
+    one = [int(b) for b in by_len if counts[b] == 1][:1]
+    tokens = sorted({int(qsl[b]) + t for b in two for t in range(2)} | {int(qsl[b]) for b in one}
+                    | {int(qsl[-1]) - 1})
+    check(x, counts, tokens=tokens)

@@ -73,3 +73,11 @@ def test_sparse_short_prefix_pads_with_minus_one():
     assert np.array_equal(np.sort(x.topk_idx[0, 0][x.topk_idx[0, 0] >= 0]), np.arange(4))
     assert np.sum(x.topk_idx[0, 0] < 0) == 4
     assert np.sum(x.topk_idx[0, 1] < 0) == 3
+
+
+def test_varlen_counts():
+    w = workload.VARLEN_SPECS["varlen_fp8_mtp2"]
+    c = workload.varlen_counts(64, w["q_len"], w["seed"])
+    assert c.shape == (64,) and c.min() >= 1 and c.max() <= w["q_len"]
+    assert set(c.tolist()) == {1, 2}
+    assert np.array_equal(c, workload.varlen_counts(64, w["q_len"], w["seed"]))

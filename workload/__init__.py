@@ -286,3 +286,18 @@ def indexer_scores(batch, q_len, context, seed, ties=False):
             x = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
         out[b] = x
     return out
+
+
+# Varlen decode: multi-token-prediction drafts give requests different query
+# counts in one call.  The spec is the fp8 mixed-length cache generated with
+# two query tokens per request; request b keeps its last counts[b] tokens,
+# counts drawn uniformly from 1 .. q_len.
+VARLEN_SPECS = {
+    "varlen_fp8_mtp2": dict(base="dense_fp8_mixed", q_len=2, seed=808),
+}
+
+
+def varlen_counts(batch, q_len, seed):
+    """Seeded query counts per request, each uniform on 1 .. q_len."""
+    rng = np.random.default_rng([seed, 11])
+    return rng.integers(1, q_len + 1, size=batch).astype(np.int64)
