@@ -307,6 +307,28 @@ int32_t mla_topk_local(const float* scores, int64_t row_stride, const int32_t* c
                        int32_t shard_count, int32_t n_shards, int32_t* cand_idx, float* cand_score,
                        void* workspace, void* stream);
 
+/* mla_topk_local for requests with different numbers of query tokens (the
+ * varlen-decode layout that multi-token prediction produces; "GLM-5.2 vLLM
+ * Decode Context Parallelism", section "See why vLLM 0.26.0 fails": the DCP
+ * backend must accept it).  Request b holds query tokens query_start_loc[b]
+ * .. query_start_loc[b + 1] - 1; with c of them, its token t is the fixed
+ * form's token t with Tq = c and selects among positions 0 .. L_b - c + t.
+ *   query_start_loc  [batch + 1] int32 on the device: 0, non-decreasing,
+ *                    last entry n_q
+ *   scores           [shard_count][n_q][row_stride] f32 (as mla_topk_local,
+ *                    one row per query token)
+ *   cand_idx         [shard_count][n_q][topk] int32 GLOBAL positions
+ *   cand_score       [shard_count][n_q][topk] f32
+ *   workspace        NULL or the error word: offsets that are not such a
+ *                    partition set MLA_DEVERR_QUERY and the tokens that
+ *                    cannot be placed select nothing (all -1)
+ * Bounds, order and exactness as mla_topk_local.  The merge takes the
+ * n_q rows as they are (mla_topk_merge with rows = n_q). */
+int32_t mla_topk_local_varlen(const float* scores, int64_t row_stride, const int32_t* context_lens,
+                              const int32_t* query_start_loc, int32_t batch, int32_t n_q, int32_t topk,
+                              int32_t shard_begin, int32_t shard_count, int32_t n_shards,
+                              int32_t* cand_idx, float* cand_score, void* workspace, void* stream);
+
 /* Merge of candidate lists into the global top-K: for each row, the topk
  * best of the union of the n_lists lists (same order as mla_topk_local), as
  * ascending positions padded with -1.  Every global top-K position is in its

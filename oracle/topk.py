@@ -93,3 +93,25 @@ def merge_topk(cand_pos, cand_score, k):
         valid = p >= 0
         out[r], _ = select(p[valid], s[valid], k)
     return out
+
+
+def local_topk_varlen(scores, context_lens, query_start_loc, k, shard, n_shards):
+    """The shard's own candidates when request b holds query tokens
+    query_start_loc[b] .. query_start_loc[b + 1] - 1 (the varlen-decode
+    layout; "GLM-5.2 vLLM Decode Context Parallelism", section "See why vLLM
+    0.26.0 fails").  Reading taken: a request with c tokens is the fixed form
+    with Tq = c, so its token t selects among positions 0 .. L_b - c + t.
+
+    scores [n_q][Lmax] float32 (global positions) -> (positions [n_q][k],
+    scores [n_q][k]) as local_topk.
+    """
+    from .decode import varlen_tokens
+    toks = varlen_tokens(query_start_loc)
+    pos = np.full((len(toks), k), -1, dtype=np.int64)
+    sc = np.full((len(toks), k), -np.inf, dtype=np.float32)
+    for i, (b, t, c) in enumerate(toks):
+        n = visible(context_lens[b], c, t)
+        owned = np.arange(shard, n, n_shards)
+        pos[i], sc[i] = select(owned, scores[i, owned], k)
+    sc[sc == 0] = 0.0
+    return pos, sc

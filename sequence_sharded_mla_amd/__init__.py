@@ -174,6 +174,19 @@ def mla_topk_local(scores, context_lens, topk, shard_begin, n_shards, cand_idx, 
         "mla_topk_local")
 
 
+
+def mla_topk_local_varlen(scores, context_lens, query_start_loc, topk, shard_begin, n_shards, cand_idx,
+                          cand_score, workspace=None, stream=None):
+    """scores [shard_count][n_q][stride] f32, request b holding query tokens
+    query_start_loc[b] .. query_start_loc[b + 1] - 1 -> cand_idx / cand_score
+    [shard_count][n_q][topk]."""
+    shard_count, n_q, stride = scores.shape
+    batch = query_start_loc.numel() - 1
+    _check(_lib.load().mla_topk_local_varlen(
+        _ptr(scores), stride, _ptr(context_lens), _ptr(query_start_loc), batch, n_q, topk, shard_begin,
+        shard_count, n_shards, _ptr(cand_idx), _ptr(cand_score), _ptr(workspace), _stream(stream)),
+        "mla_topk_local_varlen")
+
 def mla_topk_merge(cand_idx, cand_score, topk, topk_idx, stream=None):
     """cand_* [n_lists][rows][cand_k] -> topk_idx [rows][topk]."""
     n_lists = cand_idx.shape[0]

@@ -73,6 +73,8 @@ SIGNATURES = {
     "mla_dcp_kv_write": (_i32, [_vp, _i32, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _vp, _i64, _vp, _vp]),
     "mla_topk_local": (_i32, [_vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "mla_topk_local_varlen": (_i32, [_vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                     _vp, _vp]),
     "mla_topk_merge": (_i32, [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp]),
     "mla_get_device_error": (_i32, [_vp, ctypes.POINTER(_i32), _vp]),
     "mla_clear_device_error": (_i32, [_vp, _vp]),

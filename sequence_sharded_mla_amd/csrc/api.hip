@@ -348,31 +348,36 @@ int32_t mla_dcp_kv_write(const void* kv_new, int32_t src_dtype, const int32_t* r
                              per_wave > 8 ? 8 : per_wave, true, stream);
 }
 
-int32_t mla_topk_local(const float* scores, int64_t row_stride, const int32_t* context_lens,
-                       int32_t batch, int32_t q_len, int32_t topk, int32_t shard_begin,
-                       int32_t shard_count, int32_t n_shards, int32_t* cand_idx, float* cand_score,
-                       void* workspace, void* stream) {
+namespace {
+
+int32_t topk_local_impl(const float* scores, int64_t row_stride, const int32_t* context_lens,
+                        const int32_t* qsl, int32_t batch, int32_t q_len, int32_t n_q, int32_t topk,
+                        int32_t shard_begin, int32_t shard_count, int32_t n_shards, int32_t* cand_idx,
+                        float* cand_score, void* workspace, void* stream) {
     using namespace mla::topk;
-    if (batch < 0 || q_len < 1 || topk < 1 || row_stride < 1 || row_stride > kMaxLocal)
+    if (batch < 0 || n_q < 0 || topk < 1 || row_stride < 1 || row_stride > kMaxLocal)
         return MLA_ERR_SHAPE;
     if (n_shards < 1 || shard_begin < 0 || shard_count < 1 || shard_begin + shard_count > n_shards)
         return MLA_ERR_SHARD;
-    const int64_t rows = int64_t(shard_count) * batch * q_len;
+    const int64_t rows = int64_t(shard_count) * n_q;
     if (rows > INT32_MAX || rows * int64_t(topk) > (int64_t(1) << 40)) return MLA_ERR_SHAPE;
     if (rows == 0) return MLA_OK;
     if (!scores || !context_lens || !cand_idx || !cand_score) return MLA_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(scores) & 3u) || (reinterpret_cast<uintptr_t>(cand_idx) & 3u) ||
-        (reinterpret_cast<uintptr_t>(cand_score) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 3u))
+        (reinterpret_cast<uintptr_t>(cand_score) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 3u) ||
+        (reinterpret_cast<uintptr_t>(qsl) & 3u))
         return MLA_ERR_ALIGN;
     LocalParams p{};
     p.scores = scores;
     p.context_lens = context_lens;
+    p.qsl = qsl;
     p.out_idx = cand_idx;
     p.out_score = cand_score;
     p.err = static_cast<uint32_t*>(workspace);
     p.stride = row_stride;
     p.B = batch;
     p.Tq = q_len;
+    p.n_q = n_q;
     p.K = topk;
     p.shard_begin = shard_begin;
     p.n_shards = n_shards;
@@ -380,6 +385,27 @@ int32_t mla_topk_local(const float* scores, int64_t row_stride, const int32_t* c
     hipLaunchKernelGGL(local_topk_kernel, dim3(uint32_t(rows)), dim3(kThreads), size_t(words) * 8,
                        mla::as_stream(stream), p, words);
     return mla::launch_status();
+}
+
+}  // namespace
+
+int32_t mla_topk_local(const float* scores, int64_t row_stride, const int32_t* context_lens,
+                       int32_t batch, int32_t q_len, int32_t topk, int32_t shard_begin,
+                       int32_t shard_count, int32_t n_shards, int32_t* cand_idx, float* cand_score,
+                       void* workspace, void* stream) {
+    if (batch < 0 || q_len < 1 || int64_t(batch) * q_len > INT32_MAX) return MLA_ERR_SHAPE;
+    return topk_local_impl(scores, row_stride, context_lens, nullptr, batch, q_len, batch * q_len, topk,
+                           shard_begin, shard_count, n_shards, cand_idx, cand_score, workspace, stream);
+}
+
+int32_t mla_topk_local_varlen(const float* scores, int64_t row_stride, const int32_t* context_lens,
+                              const int32_t* query_start_loc, int32_t batch, int32_t n_q, int32_t topk,
+                              int32_t shard_begin, int32_t shard_count, int32_t n_shards,
+                              int32_t* cand_idx, float* cand_score, void* workspace, void* stream) {
+    if (batch < 0 || n_q < 0 || (batch == 0 && n_q != 0)) return MLA_ERR_SHAPE;
+    if (n_q > 0 && !query_start_loc) return MLA_ERR_NULL;
+    return topk_local_impl(scores, row_stride, context_lens, query_start_loc, batch, 1, n_q, topk,
+                           shard_begin, shard_count, n_shards, cand_idx, cand_score, workspace, stream);
 }
 
 int32_t mla_topk_merge(const int32_t* cand_idx, const float* cand_score, int32_t n_lists, int64_t rows,

@@ -49,13 +49,14 @@ constexpr int kStage = 32768;     // merge rows of up to kStage / 2 candidates a
 constexpr int kStageK = kCand;    // largest K the staged merge sorts in the tied-group space
 
 struct LocalParams {
-    const float* scores;     // [shard_count][B][Tq][stride]
+    const float* scores;     // [shard_count][n_q][stride], n_q = B * Tq unless varlen
     const int32_t* context_lens;
-    int32_t* out_idx;        // [shard_count][B][Tq][K]
-    float* out_score;        // [shard_count][B][Tq][K]
+    const int32_t* qsl;      // varlen: [B + 1] query offsets per request; null: Tq each
+    int32_t* out_idx;        // [shard_count][n_q][K]
+    float* out_score;        // [shard_count][n_q][K]
     uint32_t* err;           // may be null
     int64_t stride;
-    int32_t B, Tq, K, shard_begin, n_shards;
+    int32_t B, Tq, n_q, K, shard_begin, n_shards;
 };
 
 struct MergeParams {
@@ -541,6 +542,33 @@ __device__ bool select_one_pass(SelectShared& sh, SelList& buf, const Src& src, 
     return true;
 }
 
+// Request b, index t in it and its token count c of query token qi when
+// request b holds tokens qsl[b] .. qsl[b + 1] - 1.  The workgroup reads the
+// offsets together and counts those after qsl[0] that are <= qi; false when
+// the offsets are not a partition of 0 .. n_q (first 0, last n_q, none
+// decreasing).  Every thread of the workgroup must call it.
+__device__ bool varlen_token(const int32_t* qsl, int32_t B, int32_t n_q, int32_t qi, int32_t& b,
+                             int32_t& t, int32_t& c) {
+    int32_t below = 0;
+    int bad = threadIdx.x == 0 && (qsl[0] != 0 || qsl[B] != n_q);
+    for (int32_t j0 = 1; j0 <= B; j0 += kThreads) {  // the same trip count in every thread
+        const int32_t j = j0 + int32_t(threadIdx.x);
+        int le = 0;
+        if (j <= B) {
+            const int32_t v = qsl[j];
+            le = v <= qi;
+            bad |= v < qsl[j - 1];
+        }
+        below += __syncthreads_count(le);
+    }
+    if (__syncthreads_or(bad) || below >= B) return false;
+    b = below;
+    const int32_t start = qsl[b];
+    t = qi - start;
+    c = qsl[b + 1] - start;
+    return true;
+}
+
 // Local top-K of one (shard, request, query token) row.  Dynamic LDS: the
 // bitmap (one bit per local position of the longest row of the launch) and
 // the running count of set bits before each bitmap word.
@@ -551,12 +579,20 @@ __global__ void __launch_bounds__(kThreads, 4) local_topk_kernel(LocalParams p, 
     extern __shared__ uint32_t dyn[];
     uint32_t* bits = dyn;
     uint32_t* wprefix = dyn + bitmap_words;
-    const int32_t row = blockIdx.x;  // (s_rel, b, t)
-    const int32_t t = row % p.Tq;
-    const int32_t b = (row / p.Tq) % p.B;
-    const int32_t s_rel = row / (p.Tq * p.B);
+    const int32_t row = blockIdx.x;  // (s_rel, query token)
+    const int32_t s_rel = row / p.n_q;
+    const int32_t qi = row - s_rel * p.n_q;
     const int32_t s = p.shard_begin + s_rel;
-    int32_t vis = p.context_lens[b] - p.Tq + t + 1;
+    int32_t vis;
+    if (!p.qsl) {
+        const int32_t t = qi % p.Tq;
+        vis = p.context_lens[qi / p.Tq] - p.Tq + t + 1;
+    } else {
+        int32_t b, t, c;
+        vis = 0;  // a token that cannot be placed selects nothing
+        if (varlen_token(p.qsl, p.B, p.n_q, qi, b, t, c)) vis = p.context_lens[b] - c + t + 1;
+        else if (threadIdx.x == 0 && p.err) raise_error(p.err, MLA_DEVERR_QUERY);
+    }
     if (vis < 0) vis = 0;
     int64_t n = dev_local_len(vis, s, p.n_shards);
     if (n > p.stride) {  // the score row is shorter than the shard's visible prefix

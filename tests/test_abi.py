@@ -328,6 +328,23 @@ def test_topk_checks(lib):
     assert loc(ws=FAKE + 1) == _lib.MLA_ERR_ALIGN
     assert loc(B=0, sc=None) == 0
 
+    def var(sc=FAKE, stride=1000, ctx=FAKE, qsl=FAKE, B=2, nq=3, k=64, begin=0, count=8, N=8, ci=FAKE,
+            cs=FAKE, ws=None):
+        return lib.mla_topk_local_varlen(v(sc), stride, v(ctx), None if qsl is None else v(qsl), B, nq, k,
+                                         begin, count, N, v(ci), v(cs), None if ws is None else v(ws), None)
+
+    assert var(nq=-1) == _lib.MLA_ERR_SHAPE
+    assert var(B=-1) == _lib.MLA_ERR_SHAPE
+    assert var(B=0, nq=1) == _lib.MLA_ERR_SHAPE
+    assert var(stride=0) == _lib.MLA_ERR_SHAPE
+    assert var(k=0) == _lib.MLA_ERR_SHAPE
+    assert var(qsl=None) == _lib.MLA_ERR_NULL
+    assert var(qsl=FAKE + 2) == _lib.MLA_ERR_ALIGN
+    assert var(begin=1) == _lib.MLA_ERR_SHARD
+    assert var(ci=None) == _lib.MLA_ERR_NULL
+    assert var(nq=0, qsl=None, sc=None) == 0      # no query tokens: nothing to do
+    assert var(B=0, nq=0, qsl=None) == 0
+
     def mer(ci=FAKE, cs=FAKE, n=8, rows=10, ck=2048, k=2048, out=FAKE):
         return lib.mla_topk_merge(v(ci), v(cs), n, rows, ck, k, v(out), None)
 

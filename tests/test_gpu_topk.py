@@ -6,7 +6,10 @@ mla_topk_merge run through the C ABI on seeded indexer scores; the oracle
 global selection.  Cases: ragged causal prefixes (shorter than K, shorter
 than N, empty), bf16-rounded scores with many equal values, rows of equal
 scores, -inf and signed zeros, K above the LDS-resolved group, and the
-full-size selection workload on sampled rows.
+full-size selection workload on sampled rows.  The varlen call
+(mla_topk_local_varlen: a query count per request) is checked the same way,
+against the fixed form when every request is full, with more requests than
+a workgroup has threads, and with offsets that are not a partition.
 """
 
 import numpy as np
@@ -15,8 +18,9 @@ import torch
 
 import workload
 from oracle import topk as otk
-from sequence_sharded_mla_amd import (MLA_DEVERR_SCORES, layout, mla_clear_device_error,
-                                      mla_get_device_error, mla_topk_local, mla_topk_merge)
+from sequence_sharded_mla_amd import (MLA_DEVERR_QUERY, MLA_DEVERR_SCORES, layout,
+                                      mla_clear_device_error, mla_get_device_error, mla_topk_local,
+                                      mla_topk_local_varlen, mla_topk_merge)
 
 from gpu_cases import say
 
@@ -190,3 +194,82 @@ def test_merge_with_positions_beyond_the_bitmap(shuffled):
     torch.cuda.synchronize()
     ref = otk.merge_topk(ci, cs, K)
     assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def run_local_varlen(scores, lens, qsl, K, N, ws=None):
+    """scores [n_q][L] (global positions) -> device candidate lists [N][n_q][K]."""
+    n_q, L = scores.shape
+    sc_sh = layout.shard_scores(scores.reshape(n_q, 1, L), N).reshape(N, n_q, -1)
+    ci = torch.empty((N, n_q, K), dtype=torch.int32, device="cuda")
+    cs = torch.empty((N, n_q, K), dtype=torch.float32, device="cuda")
+    mla_topk_local_varlen(torch.from_numpy(np.ascontiguousarray(sc_sh)).cuda(),
+                          torch.from_numpy(np.asarray(lens, np.int32)).cuda(),
+                          torch.from_numpy(np.asarray(qsl, np.int32)).cuda(), K, 0, N, ci, cs, workspace=ws)
+    return ci, cs
+
+
+def check_varlen(scores, lens, qsl, K, N):
+    n_q = scores.shape[0]
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    ci, cs = run_local_varlen(scores, lens, qsl, K, N, ws=ws)
+    merged = torch.empty((n_q, K), dtype=torch.int32, device="cuda")
+    mla_topk_merge(ci, cs, K, merged)
+    torch.cuda.synchronize()
+    assert mla_get_device_error(ws) == 0
+    ci_h, cs_h = ci.cpu().numpy(), cs.cpu().numpy()
+    parts = [otk.local_topk_varlen(scores, lens, qsl, K, s, N) for s in range(N)]
+    for s, (ref_p, ref_s) in enumerate(parts):
+        assert np.array_equal(ci_h[s], ref_p), f"shard {s} positions"
+        assert np.array_equal(cs_h[s].view(np.uint32), ref_s.view(np.uint32)), f"shard {s} scores"
+    ref = otk.merge_topk(np.stack([p for p, _ in parts]), np.stack([q for _, q in parts]), K)
+    assert np.array_equal(merged.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("N", [1, 8])
+@pytest.mark.parametrize("K", [64, 2048])
+def test_varlen_local_and_merge_match_oracle(N, K):
+    say(f"topk varlen N={N} K={K}")
+    lens = np.array([20000, 5000, 3 * K // 2, 2, 9000])
+    counts = np.array([2, 0, 3, 1, 2])
+    qsl = np.concatenate([[0], np.cumsum(counts)])
+    n_q = int(qsl[-1])
+    scores = workload.indexer_scores(n_q, 1, 20000, seed=600 + N + K, ties=True).reshape(n_q, 20000)
+    scores[0, :500] = 0.25
+    scores[6, ::5] = -np.inf
+    check_varlen(scores, lens, qsl, K, N)
+
+
+def test_varlen_all_full_matches_fixed_form():
+    B, Tq, L, K, N = 4, 2, 30000, 2048, 8
+    lens = np.array([L, 100, 23456, 4097])
+    scores = workload.indexer_scores(B, Tq, L, seed=610)
+    ci_f, cs_f = run_local(layout.shard_scores(scores, N), lens, K, 0, N)
+    ci_v, cs_v = run_local_varlen(scores.reshape(B * Tq, L), lens, np.arange(0, B * Tq + 1, Tq), K, N)
+    torch.cuda.synchronize()
+    assert torch.equal(ci_v, ci_f.view(N, B * Tq, K))
+    assert torch.equal(cs_v.view(torch.int32), cs_f.view(N, B * Tq, K).view(torch.int32))
+
+
+def test_varlen_more_requests_than_threads():
+    """700 requests: each workgroup counts the offsets in two passes."""
+    say("topk varlen 700 requests")
+    rng = np.random.default_rng(620)
+    B, K, N = 700, 64, 4
+    lens = rng.integers(0, 3000, size=B)
+    counts = rng.integers(0, 3, size=B)
+    qsl = np.concatenate([[0], np.cumsum(counts)])
+    n_q = int(qsl[-1])
+    scores = workload.indexer_scores(n_q, 1, 3000, seed=621).reshape(n_q, 3000)
+    check_varlen(scores, lens, qsl, K, N)
+
+
+def test_varlen_offsets_not_a_partition_raise_the_error_word():
+    lens = np.array([5000, 4000, 3000])
+    scores = workload.indexer_scores(5, 1, 5000, seed=630).reshape(5, 5000)
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    for bad in ([0, 3, 2, 5], [1, 2, 3, 5], [0, 2, 3, 4]):
+        mla_clear_device_error(ws)
+        ci, cs = run_local_varlen(scores, lens, bad, 64, 4, ws=ws)
+        torch.cuda.synchronize()
+        assert mla_get_device_error(ws) & MLA_DEVERR_QUERY, bad
+        assert torch.all(ci == -1) and torch.all(torch.isneginf(cs)), bad

@@ -80,3 +80,37 @@ def test_merge_of_local_lists_is_the_global_selection(n_shards):
     # causal range: query token t of a request of length L sees L - Tq + t + 1
     assert np.all(ref[0, 0] == -1) and ref[0, 1, 0] == 0 and np.all(ref[0, 1, 1:] == -1)
     assert ref[1, 0].max() <= 698 and ref[1, 1].max() <= 699
+
+
+def test_varlen_local_lists_cover_each_tokens_causal_prefix():
+    """Varlen: request b with c tokens; its token t sees positions 0 .. L_b -
+    c + t.  With k above every prefix, a shard's list is exactly its owned
+    positions of that prefix; a request with no tokens contributes no row."""
+    lens = np.array([10, 0, 7, 3])
+    qsl = np.array([0, 3, 3, 4, 6])  # counts 3, 0, 1, 2
+    N = 3
+    sc = np.random.default_rng(5).standard_normal((6, 16)).astype(np.float32)
+    limits = [8, 9, 10, 7, 2, 3]  # visible positions per token, by hand
+    for s in range(N):
+        pos, _ = otk.local_topk_varlen(sc, lens, qsl, 16, s, N)
+        for i, v in enumerate(limits):
+            want = np.arange(s, v, N)
+            assert np.array_equal(pos[i, :want.size], want) and np.all(pos[i, want.size:] == -1)
+
+
+def test_varlen_merge_is_brute_force_top_k():
+    rng = np.random.default_rng(17)
+    lens = np.array([300, 50, 1, 220])
+    qsl = np.array([0, 2, 5, 5, 9])  # counts 2, 3, 0, 4
+    k, N = 20, 4
+    raw = rng.standard_normal((9, 300)).astype(np.float32)
+    sc = (raw.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    sc[0, :40] = 0.5  # a run of equal scores
+    parts = [otk.local_topk_varlen(sc, lens, qsl, k, s, N) for s in range(N)]
+    merged = otk.merge_topk(np.stack([p for p, _ in parts]), np.stack([s for _, s in parts]), k)
+    tok = [(0, 0, 2), (0, 1, 2), (1, 0, 3), (1, 1, 3), (1, 2, 3), (3, 0, 4), (3, 1, 4), (3, 2, 4), (3, 3, 4)]
+    for i, (b, t, c) in enumerate(tok):
+        v = max(int(lens[b]) - c + t + 1, 0)
+        best = sorted(range(v), key=lambda j: (-float(sc[i, j]), j))[:k]
+        want = sorted(best) + [-1] * (k - len(best))
+        assert list(merged[i]) == want, i
