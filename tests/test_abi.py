@@ -37,6 +37,22 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_header_is_plain_c(tmp_path):
+    """The header compiles as strict C99 and as C++ (no torch or HIP types)."""
+    import shutil
+    import subprocess
+    src = tmp_path / "use.c"
+    src.write_text('#include "mla_dcp.h"\nint main(void) { return (int)sizeof(mla_decode_desc) > 0 ? 0 : 1; }\n')
+    for cc, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not available")
+        lang = ["-x", "c++"] if cc == "g++" else []
+        res = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", *lang, "-I",
+                              os.path.dirname(HDR), "-c", str(src), "-o", str(tmp_path / "use.o")],
+                             capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr
+
+
 def test_status_strings(lib):
     for code in range(8):
         s = lib.mla_status_string(code)
