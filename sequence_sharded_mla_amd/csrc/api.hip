@@ -125,7 +125,7 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     }
     if ((st = launch_status()) != MLA_OK) return st;
     if (plan.planned) {
-        hipLaunchKernelGGL(chunk_combine_kernel, dim3(uint32_t(plan.rows), uint32_t(d->num_heads)),
+        hipLaunchKernelGGL(chunk_combine_kernel, dim3(uint32_t(plan.rows), uint32_t((d->num_heads + 3) / 4)),
                            dim3(256), 0, s, p);
         if ((st = launch_status()) != MLA_OK) return st;
     }

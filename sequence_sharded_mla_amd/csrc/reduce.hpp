@@ -170,12 +170,10 @@ __device__ __forceinline__ void accumulate_parts(const T* base, size_t part_stri
     }
 }
 
-// Partials of split rows -> that shard's O_partial / LSE.  grid = (rows, H),
-// 256 threads, one head per workgroup; rows of one item were written
-// directly.  A row of at most 64 parts is merged by one wave.  A longer row
-// (a few very long rows split into many chunks) has its parts dealt to the
-// four waves in contiguous quarters; the waves' sums meet in LDS and are
-// added in wave order, so the result is reproducible bit for bit.
+// One head of a row with more than 64 partials (a few very long rows split
+// into many chunks): its parts are dealt to the four waves in contiguous
+// quarters; the waves' sums meet in LDS and are added in wave order, so the
+// result is reproducible bit for bit.  Every thread of the workgroup calls it.
 template <typename T>
 __device__ __forceinline__ void combine_head(const DecodeParams& p, int row, int h, int32_t slot0,
                                              int32_t k) {
@@ -187,12 +185,6 @@ __device__ __forceinline__ void combine_head(const DecodeParams& p, int row, int
     const T* o = static_cast<const T*>(p.ws_o) + s0 * kLatent;
     const float* lse = p.ws_lse + s0;
     const size_t stride = size_t(p.H);
-    if (k <= 64) {
-        if (wave == 0)
-            merge_wave<T>(k, o, stride * kLatent, lse, stride, p.o_out, p.out_dtype, head * kLatent,
-                          p.lse_out + head, lane);
-        return;
-    }
     float M = -INFINITY;  // every wave finds the same maximum
     for (int j = lane; j < k; j += 64) M = fmaxf(M, lse[size_t(j) * stride]);
     M = wave_max(M);
@@ -206,19 +198,41 @@ __device__ __forceinline__ void combine_head(const DecodeParams& p, int row, int
     for (int e = 0; e < 8; ++e) part_acc[wave][lane][e] = acc[e];
     if (lane == 0) part_w[wave] = W;
     __syncthreads();
-    if (wave != 0) return;
-    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float Wt = 0.f;
-    for (int w = 0; w < 4; ++w) {
+    if (wave == 0) {
+        float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float Wt = 0.f;
+        for (int w = 0; w < 4; ++w) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum[e] += part_acc[w][lane][e];
-        Wt += part_w[w];
+            for (int e = 0; e < 8; ++e) sum[e] += part_acc[w][lane][e];
+            Wt += part_w[w];
+        }
+        const float inv = Wt > 0.f ? 1.f / Wt : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] *= inv;
+        store8(p.o_out, p.out_dtype, head * kLatent + lane * 8, sum);
+        if (lane == 0) p.lse_out[head] = (M == -INFINITY) ? -INFINITY : M + logf(Wt);
     }
-    const float inv = Wt > 0.f ? 1.f / Wt : 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sum[e] *= inv;
-    store8(p.o_out, p.out_dtype, head * kLatent + lane * 8, sum);
-    if (lane == 0) p.lse_out[head] = (M == -INFINITY) ? -INFINITY : M + logf(Wt);
+    __syncthreads();  // part_acc is free for the next head
+}
+
+// Chunk combine of a planned step (partials of split rows -> that shard's
+// O_partial / LSE; rows of one item were written directly): grid = (rows,
+// ceil(H / 4)), 256 threads; workgroup (row, y) owns heads 4y .. 4y + 3.  Up to 64 partials per row, wave w merges head 4y + w on
+// its own; more than that, the four waves split each head's partials in turn.
+template <typename T>
+__device__ __forceinline__ void combine_heads(const DecodeParams& p, int row, int32_t slot0, int32_t k) {
+    const int h0 = 4 * int(blockIdx.y);
+    const int h_end = min(h0 + 4, p.H);
+    if (k <= 64) {
+        const int h = h0 + int(threadIdx.x >> 6);
+        if (h >= h_end) return;
+        const size_t head = size_t(row) * p.H + h;
+        const size_t s0 = size_t(slot0) * p.H + h;
+        merge_wave<T>(k, static_cast<const T*>(p.ws_o) + s0 * kLatent, size_t(p.H) * kLatent, p.ws_lse + s0,
+                      size_t(p.H), p.o_out, p.out_dtype, head * kLatent, p.lse_out + head, threadIdx.x & 63);
+        return;
+    }
+    for (int h = h0; h < h_end; ++h) combine_head<T>(p, row, h, slot0, k);
 }
 
 __global__ void __launch_bounds__(256) chunk_combine_kernel(DecodeParams p) {
@@ -227,9 +241,9 @@ __global__ void __launch_bounds__(256) chunk_combine_kernel(DecodeParams p) {
     const int32_t k = p.row_info[2 * size_t(row) + 1];
     if (k <= 1) return;
     if (p.out_dtype == MLA_F32)
-        combine_head<float>(p, row, blockIdx.y, slot0, k);
+        combine_heads<float>(p, row, slot0, k);
     else
-        combine_head<uint16_t>(p, row, blockIdx.y, slot0, k);
+        combine_heads<uint16_t>(p, row, slot0, k);
 }
 
 constexpr int kPlanThreads = 256;
