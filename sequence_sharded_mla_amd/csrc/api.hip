@@ -125,8 +125,13 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     }
     if ((st = launch_status()) != MLA_OK) return st;
     if (plan.planned) {
-        hipLaunchKernelGGL(chunk_combine_kernel, dim3(uint32_t(plan.rows), uint32_t((d->num_heads + 3) / 4)),
-                           dim3(256), 0, s, p);
+        // chunks of a row <= its local tokens / the smallest chunk size: when no
+        // row can pass 64 partials, a wave per head and four heads per
+        // workgroup; else one head per workgroup for the four-wave split
+        const int64_t max_chunks = (int64_t(d->max_blocks) * mla::kBlock + plan.chunk_min - 1) / plan.chunk_min;
+        const int hpw = max_chunks <= 64 ? 4 : 1;
+        hipLaunchKernelGGL(chunk_combine_kernel, dim3(uint32_t(plan.rows), uint32_t((d->num_heads + hpw - 1) / hpw)),
+                           dim3(256), 0, s, p, hpw);
         if ((st = launch_status()) != MLA_OK) return st;
     }
     return MLA_OK;

@@ -217,12 +217,15 @@ __device__ __forceinline__ void combine_head(const DecodeParams& p, int row, int
 
 // Chunk combine of a planned step (partials of split rows -> that shard's
 // O_partial / LSE; rows of one item were written directly): grid = (rows,
-// ceil(H / 4)), 256 threads; workgroup (row, y) owns heads 4y .. 4y + 3.  Up to 64 partials per row, wave w merges head 4y + w on
-// its own; more than that, the four waves split each head's partials in turn.
+// ceil(H / hpw)), 256 threads; workgroup (row, y) owns heads hpw * y ..
+// hpw * y + hpw - 1, hpw = 4 when no row can have more than 64 partials,
+// else 1.  Up to 64 partials per row, wave w merges head hpw * y + w on its
+// own; more than that, the four waves split each head's partials in turn.
 template <typename T>
-__device__ __forceinline__ void combine_heads(const DecodeParams& p, int row, int32_t slot0, int32_t k) {
-    const int h0 = 4 * int(blockIdx.y);
-    const int h_end = min(h0 + 4, p.H);
+__device__ __forceinline__ void combine_heads(const DecodeParams& p, int row, int32_t slot0, int32_t k,
+                                              int hpw) {
+    const int h0 = hpw * int(blockIdx.y);
+    const int h_end = min(h0 + hpw, p.H);
     if (k <= 64) {
         const int h = h0 + int(threadIdx.x >> 6);
         if (h >= h_end) return;
@@ -235,15 +238,15 @@ __device__ __forceinline__ void combine_heads(const DecodeParams& p, int row, in
     for (int h = h0; h < h_end; ++h) combine_head<T>(p, row, h, slot0, k);
 }
 
-__global__ void __launch_bounds__(256) chunk_combine_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(256) chunk_combine_kernel(DecodeParams p, int hpw) {
     const int row = blockIdx.x;
     const int32_t slot0 = p.row_info[2 * size_t(row)];  // a row's slots are consecutive
     const int32_t k = p.row_info[2 * size_t(row) + 1];
     if (k <= 1) return;
     if (p.out_dtype == MLA_F32)
-        combine_heads<float>(p, row, slot0, k);
+        combine_heads<float>(p, row, slot0, k, hpw);
     else
-        combine_heads<uint16_t>(p, row, slot0, k);
+        combine_heads<uint16_t>(p, row, slot0, k, hpw);
 }
 
 constexpr int kPlanThreads = 256;
