@@ -227,3 +227,31 @@ def test_varlen_sparse_and_token_subset():
         decode.mla_decode_varlen(q, rows, np.array(lens), qsl, N, SCALE, topk_idx=bad)
     with pytest.raises(ValueError):
         decode.mla_decode_varlen(q, rows, np.array(lens), np.array([0, 3, 2]), N, SCALE)
+
+
+def test_sparse_repeated_positions_count_with_multiplicity():
+    """Reading taken: a top-K list is a multiset, one softmax term per entry.
+    Closed form: one position listed m times gives its latent as O and
+    s + ln m as LSE.  In general, a position listed m times equals the same
+    key listed once with ln m added to its score (scipy's logsumexp over the
+    distinct keys with those weights)."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(8)
+    L, N, H = 50, 3, 2
+    q, store, rows = _make(rng, 1, 2, H, [L])
+    idx = np.array([[[7, 7, 7, 7, 7, -1], [4, 9, 9, 20, 4, 4]]], dtype=np.int32)
+    r = decode.mla_decode(q, rows, np.array([L]), 2, N, SCALE, topk_idx=idx)
+    s7 = SCALE * (q[0, 0] @ store[0][7])
+    assert np.allclose(r["o"][0, 0], np.broadcast_to(store[0][7, :512], (H, 512)), atol=1e-13)
+    assert np.allclose(r["lse"][0, 0], s7 + np.log(5.0), atol=1e-13)
+    keys, mult = np.array([4, 9, 20]), np.array([3.0, 2.0, 1.0])
+    s = SCALE * (q[0, 1] @ store[0][keys].T) + np.log(mult)[None, :]
+    lse = logsumexp(s, axis=1)
+    o = np.exp(s - lse[:, None]) @ store[0][keys][:, :512]
+    assert np.allclose(r["lse"][0, 1], lse, atol=1e-12)
+    assert np.allclose(r["o"][0, 1], o, atol=1e-12)
+    # the shard owning position 4 (4 mod 3 = 1) counts it three times
+    k4 = store[0][[4]]
+    o1, l1 = attention.attend(q[0, 1], k4, k4[:, :512], SCALE)
+    assert np.allclose(r["lse_shards"][1, 0, 1], l1 + np.log(3.0), atol=1e-12)
+    assert np.allclose(r["o_shards"][1, 0, 1], o1, atol=1e-13)
