@@ -119,6 +119,42 @@ def copy_rate_gbs(reps=5):
     return 2 * n / (float(np.median(ts)) * 1e-3) / 1e9
 
 
+def stream_read_gbs(reps=7, nbytes=4 << 30, grid=16384):
+    """HBM streaming-read reference measured in the same run: bytes per
+    second a read-only kernel (libmla_hbm_probe.so: 16-byte non-temporal
+    loads, eight in flight per thread, 16384 workgroups) reaches over a 4 GiB
+    buffer.  Returns (median, best) GB/s over `reps` launches."""
+    import ctypes
+    import torch
+    from sequence_sharded_mla_amd.build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    fn = lib.mla_hbm_read_probe
+    fn.restype = ctypes.c_int32
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        if fn(buf.data_ptr(), nbytes, grid, sink.data_ptr(), stream.cuda_stream) != 0:
+            raise RuntimeError("mla_hbm_read_probe failed")
+    launch()
+    torch.cuda.synchronize()
+    ts = time_launches(launch, reps, stream)
+    del buf
+    return nbytes / (float(np.median(ts)) * 1e-3) / 1e9, nbytes / (float(ts.min()) * 1e-3) / 1e9
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(x, budget_s=10.0):
     """Time the float64 oracle (shard partials + merge) on whole requests."""
     from threadpoolctl import threadpool_info
@@ -143,18 +179,24 @@ def cpu_baseline(x, budget_s=10.0):
     kv_bytes = tokens * ROW_BYTES[sp.kv_dtype]
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s",
             "kv_tokens_per_s": round(tokens / dt, 1), "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{done} of {sp.batch} requests (all {sp.n_shards} shards + merge), "
                       f"{tokens} attended tokens, {dt:.1f} s"}
 
 
-def traffic_for(workload, khash):
+def profile_record(workload, khash):
+    """The committed counter record of a workload (profiles/traffic_*.json),
+    or None when the kernel sources have changed since it was taken."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    if rec.get("kernel_hash") != khash:
-        return None
-    return rec.get("bytes_per_launch")
+    return rec if rec.get("kernel_hash") == khash else None
+
+
+def traffic_for(workload, khash):
+    rec = profile_record(workload, khash)
+    return None if rec is None else rec.get("bytes_per_launch")
 
 
 def write_bytes_per_token(src_dtype, kv_dtype):
@@ -543,6 +585,8 @@ def main():
                          "copy series")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only run the 4 GiB streaming-read probe three times (counter reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -558,6 +602,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.stream_probe:
+        med, best = stream_read_gbs(reps=3)
+        print(json.dumps({"stream_probe_bytes": 4 << 30, "launches": 5, "median_gbs": round(med, 1),
+                          "best_gbs": round(best, 1)}), flush=True)
         return
     if args.kv_write:
         run_kv_write(args)
@@ -590,13 +639,19 @@ def main():
     torch.cuda.synchronize()
     assert mla_get_device_error(step.workspace) == 0
 
+    # Timed region: K steps, each after a 1 GiB fill (outside its events) that
+    # evicts the 256 MB last-level cache, so no cache row of the previous step
+    # is served from it.  The step's time is its own events (partials, then
+    # merge); the fills run on the same stream between them.
     K = args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    log(f"bench: timing {K} steps")
+    evict = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    log(f"bench: timing {K} steps (cache flushed before each)")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
+        evict.fill_(i & 0xff)
         a, b, c = ev[i]
         a.record(stream)
         step.partials()
@@ -605,30 +660,38 @@ def main():
         c.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / K
     t_part = np.array([e[0].elapsed_time(e[1]) for e in ev])
     t_merge = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    t_step = t_part + t_merge
+    ms_per_step = float(np.mean(t_step))
+    del evict
     assert mla_get_device_error(step.workspace) == 0
 
     extras = not args.no_extras
-    # Cold-cache series (not the timed region): a 1 GiB fill before every
-    # step evicts the 256 MB last-level cache, so no KV row of the previous
-    # step is served from it; only the events around the launches count.
-    evict = torch.empty(1 << 30 if extras else 1, dtype=torch.uint8, device="cuda")
-    cold = []
-    for i in range(K if extras else 0):
-        evict.fill_(i & 0xff)
-        a, b, c = ev[i]
-        a.record(stream)
-        step.partials()
-        b.record(stream)
-        step.merge()
-        c.record(stream)
+    # Warm series (secondary): K steps back to back, no flush.
+    warm = None
+    if extras:
+        ev_w = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                 torch.cuda.Event(enable_timing=True)) for _ in range(K)]
         torch.cuda.synchronize()
-        cold.append((a.elapsed_time(b), b.elapsed_time(c)))
-    cold = np.array(cold).reshape(-1, 2)
-    del evict
-    assert mla_get_device_error(step.workspace) == 0
+        tw0 = time.perf_counter()
+        for a, b, c in ev_w:
+            a.record(stream)
+            step.partials()
+            b.record(stream)
+            step.merge()
+            c.record(stream)
+        torch.cuda.synchronize()
+        wall_w = time.perf_counter() - tw0
+        tw_part = np.array([e[0].elapsed_time(e[1]) for e in ev_w])
+        tw_merge = np.array([e[1].elapsed_time(e[2]) for e in ev_w])
+        warm = {"note": "back-to-back steps, no flush; wall-clock per step includes launch gaps",
+                "ms_per_step_wall": round(wall_w * 1e3 / K, 4),
+                "decode_partials_mean_ms": round(float(np.mean(tw_part)), 4),
+                "decode_partials_median_ms": round(float(np.median(tw_part)), 4),
+                "lse_merge_mean_ms": round(float(np.mean(tw_merge)), 4),
+                "decode_frac": round(launch_bytes / (float(np.mean(tw_part)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        assert mla_get_device_error(step.workspace) == 0
 
     # One shard's call, the launch one DCP rank makes for its share of the
     # cache (shard 0, its own block table and workspace).
@@ -646,21 +709,39 @@ def main():
     for _ in range(3 if extras else 0):
         one_shard()
     torch.cuda.synchronize()
-    t_one = []
-    for i in range(K if extras else 0):
-        a, b, _ = ev[i]
-        a.record(stream)
-        one_shard()
-        b.record(stream)
-    torch.cuda.synchronize()
-    t_one = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K if extras else 0)])
+    t_one = time_launches(one_shard, K, stream) if extras else np.array([np.nan])
     assert mla_get_device_error(ws1) == 0
     one_bytes, one_tokens = shard_bytes(x, 0, out_b, q_b)
 
-    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    from sequence_sharded_mla_amd.layout import ROW_BYTES
+    kv_bytes = tokens * ROW_BYTES[sp.kv_dtype]
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     part_ms = float(np.mean(t_part))
     achieved = launch_bytes / (part_ms * 1e-3) / 1e9
     khash = kernel_hash()
+    prof = profile_record(sp.name, khash)
+    stream_med = stream_best = None
+    if extras:
+        stream_med, stream_best = stream_read_gbs()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None if prof is None else prof.get("bytes_per_launch"),
+                "kernel": "decode partials (all shards, one launch), flushed-cache steps, HIP events",
+                "algorithmic_bytes_per_launch": int(launch_bytes),
+                "decode_launch_mean_ms": round(part_ms, 4),
+                "decode_launch_median_ms": round(float(np.median(t_part)), 4),
+                "decode_launch_p10_p90_ms": [round(float(np.percentile(t_part, 10)), 4),
+                                             round(float(np.percentile(t_part, 90)), 4)]}
+    if stream_med:
+        roofline["stream_read_gbs"] = round(stream_med, 1)
+        roofline["frac_of_stream_read"] = round(achieved / stream_med, 4)
+    if prof is not None and prof.get("kernel_avg_ns"):
+        # the decode kernel alone, from the committed rocprofv3 trace of the
+        # same kernel sources (kernel_hash)
+        k_gbs = prof["kernel_bytes_per_launch"] / (prof["kernel_avg_ns"] * 1e-9) / 1e9
+        roofline["profile_kernel"] = {"kernel": prof.get("kernel"), "avg_us": round(prof["kernel_avg_ns"] / 1e3, 1),
+                                      "achieved_gbs": round(k_gbs, 1), "frac": round(k_gbs / PEAK_HBM_GBS, 4),
+                                      "source": prof.get("source")}
     rec = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -668,7 +749,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -677,38 +758,36 @@ def main():
         "config": {"workload": sp.name, "batch": sp.batch, "q_len": sp.q_len, "heads": sp.heads,
                    "context": sp.context or list(sp.ctx_range), "n_shards": sp.n_shards,
                    "kv_cache": sp.kv_dtype, "topk": sp.topk, "block_size": 64},
+        "timing": "each step after a 1 GiB cache flush; ms_per_step = mean of the steps' HIP-event "
+                  "times (partials + merge)",
+        "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 4),
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
-        "kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "kv_tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
+        "kv_only_gbs": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "algorithmic_bytes_per_step": int(step_bytes),
         "kernels_ms": {"decode_partials": round(part_ms, 4),
                        "decode_partials_median": round(float(np.median(t_part)), 4),
                        "decode_partials_p10_p90": [round(float(np.percentile(t_part, 10)), 4),
                                                    round(float(np.percentile(t_part, 90)), 4)],
-                       "lse_merge": round(float(np.mean(t_merge)), 4)},
-        "cold_cache": None if not extras else {
-            "note": "1 GiB fill before each step (outside the events)",
-            "decode_partials_median_ms": round(float(np.median(cold[:, 0])), 4),
-            "lse_merge_median_ms": round(float(np.median(cold[:, 1])), 4),
-            "decode_frac": round(launch_bytes / (float(np.median(cold[:, 0])) * 1e-3) / 1e9
-                                 / PEAK_HBM_GBS, 4)},
+                       "lse_merge": round(float(np.mean(t_merge)), 4),
+                       "step_median": round(float(np.median(t_step)), 4)},
+        "warm": warm,
         "single_shard": None if not extras else {
-            "note": "mla_decode_partial for shard 0 of the same cache (one rank's call)",
+            "note": "mla_decode_partial for shard 0 of the same cache (one rank's call), back to back",
             "median_ms": round(float(np.median(t_one)), 4),
             "algorithmic_bytes": int(one_bytes), "kv_tokens": one_tokens,
             "achieved_gbs": round(one_bytes / (float(np.median(t_one)) * 1e-3) / 1e9, 2),
             "frac": round(one_bytes / (float(np.median(t_one)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_for(sp.name, khash),
-                     "kernel": "decode partials (all shards, one launch)",
-                     "algorithmic_bytes_per_launch": int(launch_bytes)},
+        "roofline": roofline,
         "kernel_hash": khash,
     }
     if extras:
         copy_gbs = copy_rate_gbs()
         rec["hbm_reference"] = {"copy_gbs": round(copy_gbs, 1),
-                                "note": "1 GiB device copy in the same run, read + write bytes",
-                                "decode_frac_of_copy": round(achieved / copy_gbs, 4)}
+                                "stream_read_gbs": round(stream_med, 1),
+                                "stream_read_best_gbs": round(stream_best, 1),
+                                "note": "same run: a 1 GiB device copy (read + write bytes) and the "
+                                        "streaming-read probe over 4 GiB (read bytes)"}
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host")
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)

@@ -47,7 +47,10 @@
  *                (0 <= t < Tq) sits at global position L_b - Tq + t and
  *                attends positions 0 .. L_b - Tq + t
  *   topk_idx     [B][Tq][topk] int32 GLOBAL positions (negative = unused);
- *                a shard attends only the entries it owns (sparse mode)
+ *                a shard attends only the entries it owns (sparse mode).
+ *                The list is a multiset: every non-negative entry is one
+ *                term of the softmax, so a position listed twice is attended
+ *                twice (weight 2 exp(s) in the normaliser and in the output)
  *   o_partial    [B*Tq][H][512] out_dtype     (token/head form)
  *   lse          [B*Tq][H] f32, natural log of sum exp(scale * q.k)
  *
@@ -129,7 +132,14 @@ int64_t mla_kv_row_bytes(int32_t kv_dtype);
  * mla_decode_partial_shards (shard_count shards) needs for `desc`.  Pure host
  * function: validates desc (same checks and codes as the decode calls) and
  * writes the size to *bytes_out.  The size is at least 256 (the device error
- * word lives in the first 4 bytes). */
+ * word lives in the first 4 bytes).  Beyond the error word the workspace
+ * holds the step's transient state: the chunk plan and the float32 partial
+ * outputs of rows split into chunks (their combine is the LSE merge below),
+ * bounded by desc alone, so a caller can reserve it once, apart from the
+ * cache pool.  Keeping the attention workspace a known, separately measured
+ * allocation is what "GLM-5.2 vLLM Decode Context Parallelism", section
+ * "Measure capacity and service behavior" asks for after a decode OOM inside
+ * the attention kernel's own workspace. */
 int32_t mla_decode_workspace_size(const mla_decode_desc* desc, int32_t shard_count,
                                   int64_t* bytes_out);
 
@@ -301,7 +311,9 @@ int32_t mla_dcp_kv_write(const void* kv_new, int32_t src_dtype, const int32_t* r
  *   workspace   NULL or a buffer whose first 32-bit word is the error word:
  *               a row_stride shorter than a shard's visible prefix sets
  *               MLA_DEVERR_SCORES and only the first row_stride entries count
- * 1 <= row_stride <= 2^19, topk >= 1, scores 4-byte aligned.  Bit-exact. */
+ * 1 <= row_stride <= 393216 (the selection keeps a bitmap of the row's
+ * positions in LDS beside its other state; MLA_ERR_SHAPE above), topk >= 1,
+ * scores 4-byte aligned.  Bit-exact. */
 int32_t mla_topk_local(const float* scores, int64_t row_stride, const int32_t* context_lens,
                        int32_t batch, int32_t q_len, int32_t topk, int32_t shard_begin,
                        int32_t shard_count, int32_t n_shards, int32_t* cand_idx, float* cand_score,
@@ -342,7 +354,13 @@ int32_t mla_topk_merge(const int32_t* cand_idx, const float* cand_score, int32_t
                        int32_t cand_k, int32_t topk, int32_t* topk_idx, void* stream);
 
 /* Read the device error word of a workspace: waits for `stream`, then copies
- * the word to *code_out (0 = no error; else MLA_DEVERR_* bits). */
+ * the word to *code_out (0 = no error; else MLA_DEVERR_* bits).  A block
+ * table narrower than a request's local length is reported here as
+ * MLA_DEVERR_BLOCK_TABLE instead of being copied past its end: the table
+ * width a shard needs depends on the DCP factor, and a width mismatch is a
+ * failure signature of its own ("GLM-5.2 vLLM Decode Context Parallelism",
+ * section "Measure capacity and service behavior").  Host function; the
+ * workspace pointer is a device pointer. */
 int32_t mla_get_device_error(const void* workspace, int32_t* code_out, void* stream);
 
 /* Enqueue a reset of the device error word to 0 on `stream`. */

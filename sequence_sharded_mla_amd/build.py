@@ -23,17 +23,28 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    """Compile every source into sequence_sharded_mla_amd/libmla_dcp.so."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-o", tmp] + SOURCES
+# the bench's streaming-read reference (not part of the decode library)
+PROBE_LIB = os.path.join(PKG, "libmla_hbm_probe.so")
+PROBE_SOURCES = [os.path.join(PKG, "csrc", "hbm_probe.hip")]
+
+
+def _compile(lib, sources, verbose):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC] + FLAGS + ["-o", tmp] + sources
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libmla_dcp.so")
+        raise RuntimeError(f"hipcc failed building {os.path.basename(lib)}")
     if verbose:
         sys.stdout.write(res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compile libmla_dcp.so (every decode-library source) and the bench's
+    libmla_hbm_probe.so in-tree."""
+    _compile(LIB, SOURCES, verbose)
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose)
     return LIB
 
 

@@ -22,14 +22,17 @@ int32_t launch_status() {
 }
 
 // qsl: null (q_len query tokens per request), or the varlen query offsets
-// [batch + 1] with n_q query tokens in all.
+// [batch + 1] with n_q query tokens in all.  ws_cap > 0: the plan must fit in
+// ws_cap bytes of workspace (the allocation-free call's scratch).  err_word:
+// the device error word, or null for the workspace's first word.
 int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool,
                     const int32_t* block_tables, const int32_t* context_lens,
                     const int32_t* topk_idx, int32_t shard_begin, int32_t shard_count,
                     int32_t n_shards, void* o, float* lse, void* ws, int64_t ws_bytes,
-                    void* stream, const int32_t* qsl = nullptr, int32_t n_q = -1) {
+                    void* stream, const int32_t* qsl = nullptr, int32_t n_q = -1,
+                    int64_t ws_cap = -1, uint32_t* err_word = nullptr) {
     Plan plan;
-    int32_t st = make_plan(d, shard_count, &plan, n_q);
+    int32_t st = make_plan(d, shard_count, &plan, n_q, ws_cap);
     if (st != MLA_OK) return st;
     if (qsl && (reinterpret_cast<uintptr_t>(qsl) & 3u)) return MLA_ERR_ALIGN;
     if (n_shards < 1 || n_shards > 4096 || shard_begin < 0 || shard_begin + shard_count > n_shards)
@@ -38,7 +41,7 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     if (d->topk > 0 && !topk_idx) return MLA_ERR_NULL;
     if (d->topk == 0 && topk_idx) return MLA_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(o) || !aligned16(ws) ||
-        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(err_word) & 3u))
         return MLA_ERR_ALIGN;
     if (ws_bytes < plan.ws_bytes) return MLA_ERR_WORKSPACE;
     if (d->batch == 0 || plan.n_q == 0) return MLA_OK;
@@ -52,12 +55,12 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     p.o_out = o;
     p.lse_out = lse;
     uint8_t* w = static_cast<uint8_t*>(ws);
-    p.err = reinterpret_cast<uint32_t*>(w);
+    p.err = err_word ? err_word : reinterpret_cast<uint32_t*>(w);
     p.plan_hdr = reinterpret_cast<const int32_t*>(w);
     if (plan.planned) {
         p.items = reinterpret_cast<const int32_t*>(w + plan.items_off);
         p.row_info = reinterpret_cast<const int32_t*>(w + plan.row_info_off);
-        p.ws_o = w + plan.ws_o_off;
+        p.ws_o = reinterpret_cast<float*>(w + plan.ws_o_off);
         p.ws_lse = reinterpret_cast<float*>(w + plan.ws_lse_off);
     }
     p.pool_blocks = d->pool_blocks;

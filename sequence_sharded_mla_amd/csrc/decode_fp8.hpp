@@ -271,76 +271,101 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     const uint32_t ls0 = __builtin_amdgcn_readfirstlane(lds_addr(sm.scl) + wv * kSclRows * 16);
 
     bool bad_slot[kRingF] = {false, false, false};
-    auto issue = [&](int j, auto slot_c) {
+    // Source of sub-tile j.  Dense: first row in HBM (the zero row for a
+    // padding or bad sub-tile); sparse: the list entries from j0.  Rows past
+    // `last` re-read row `last`.
+    struct SrcF {
+        const uint8_t* src;
+        int32_t j0;
+        int last;
+        int v;  // real rows (<= 0: padding)
+        bool full;
+    };
+    // block id of dense sub-tile j (-1 past the range, whose entry is not
+    // read).  The main loop reads it one iteration ahead, at a point where no
+    // LDS read is in flight, so that waiting for it waits for nothing else.
+    auto block_of = [&](int j) -> int32_t {
+        const int32_t j0 = tok0 + j * kSub;
+        return (!SPARSE && j0 < tok1) ? btc[uint32_t(j0) / kBlock] : -1;
+    };
+    auto prep = [&](int j, int32_t blk, auto slot_c) -> SrcF {
         constexpr int slot = decltype(slot_c)::value;
-        // opaque copies: the per-load offsets below are then computed here,
-        // not hoisted out of the loop into a dozen live registers
-        int c_x = c_x0, c_h = c_h0, r_x = r_x0, r_h = r_h0, s_row = s_row0;
-        asm volatile("" : "+v"(c_x), "+v"(c_h), "+v"(r_x), "+v"(r_h), "+v"(s_row));
         const int32_t j0 = tok0 + j * kSub;
         const int v = min(kSub, tok1 - j0);  // <= 0: padding
+        SrcF r{kZeroRow, j0, (v > 0 ? v : 1) - 1, v, false};
         if (!SPARSE) {
-            const uint8_t* src = kZeroRow;
             bool bad = false;
-            int last = 0;
+            r.last = 0;
             if (v > 0) {
-                const int32_t blk = btc[uint32_t(j0) / kBlock];
                 if (blk >= 0 && blk < p.pool_blocks) {
-                    src = p.kv + (int64_t(blk) * kBlock + (uint32_t(j0) % kBlock)) * kRowF;
-                    last = v - 1;
+                    r.src = p.kv + (int64_t(blk) * kBlock + (uint32_t(j0) % kBlock)) * kRowF;
+                    r.last = v - 1;
+                    r.full = v == kSub;
                 } else {
                     bad = true;
                 }
             }
             bad_slot[slot] = bad;
-            if (v == kSub && !bad) {
-                static_for<0, kCodeLoads>([&](auto kc) {
-                    constexpr int k = decltype(kc)::value;
-                    dma16_at<slot * kCodesB + k * 1024>(src, (c_x ^ (u_bits(k) << 4)) + c_h + 2 * k * kRowF,
+        }
+        return r;
+    };
+    // Load kk of this wave for the sub-tile of r in `slot`: kk < kCodeLoads a
+    // code load, then kRopeLoads rope loads, then the scale load.
+    auto load_one = [&](const SrcF& r, auto slot_c, auto kk_c) {
+        constexpr int slot = decltype(slot_c)::value;
+        constexpr int kk = decltype(kk_c)::value;
+        // opaque copies: the per-load offsets below are then computed here,
+        // not hoisted out of the loop into a dozen live registers
+        int c_x = c_x0, c_h = c_h0, r_x = r_x0, r_h = r_h0, s_row = s_row0;
+        asm volatile("" : "+v"(c_x), "+v"(c_h), "+v"(r_x), "+v"(r_h), "+v"(s_row));
+        if constexpr (!SPARSE) {
+            if constexpr (kk < kCodeLoads) {
+                constexpr int k = kk;
+                if (r.full) {
+                    dma16_at<slot * kCodesB + k * 1024>(r.src, (c_x ^ (u_bits(k) << 4)) + c_h + 2 * k * kRowF,
                                                         lc0);
-                });
-                static_for<0, kRopeLoads>([&](auto kc) {
-                    constexpr int k = decltype(kc)::value;
-                    dma16_at<slot * kRopeSB + k * 1024>(src, (r_x ^ ((4 * (k & 1)) << 4)) + r_h + 8 * k * kRowF,
-                                                        lr0);
-                });
-                if (lane < kSclRows) dma16_at<slot * kSclB>(src, s_row * kRowF + kScaleOff, ls0);
-            } else {
-                // rows past `last` re-read row `last`
-                static_for<0, kCodeLoads>([&](auto kc) {
-                    constexpr int k = decltype(kc)::value;
+                } else {
                     const int t = 2 * (wv * kCodeLoads + k) + h;
                     dma16_at<slot * kCodesB + k * 1024>(
-                        src, (c_x ^ (u_bits(k) << 4)) + (t < last ? t : last) * kRowF, lc0);
-                });
-                static_for<0, kRopeLoads>([&](auto kc) {
-                    constexpr int k = decltype(kc)::value;
+                        r.src, (c_x ^ (u_bits(k) << 4)) + (t < r.last ? t : r.last) * kRowF, lc0);
+                }
+            } else if constexpr (kk < kCodeLoads + kRopeLoads) {
+                constexpr int k = kk - kCodeLoads;
+                if (r.full) {
+                    dma16_at<slot * kRopeSB + k * 1024>(r.src, (r_x ^ ((4 * (k & 1)) << 4)) + r_h + 8 * k * kRowF,
+                                                        lr0);
+                } else {
                     const int t = 8 * (wv * kRopeLoads + k) + rr;
                     dma16_at<slot * kRopeSB + k * 1024>(
-                        src, (r_x ^ ((4 * (k & 1)) << 4)) + kRopeOff + (t < last ? t : last) * kRowF, lr0);
-                });
-                const int t = s_row < last ? s_row : last;
-                if (lane < kSclRows) dma16_at<slot * kSclB>(src, t * kRowF + kScaleOff, ls0);
+                        r.src, (r_x ^ ((4 * (k & 1)) << 4)) + kRopeOff + (t < r.last ? t : r.last) * kRowF, lr0);
+                }
+            } else {
+                const int t = (r.full || s_row < r.last) ? s_row : r.last;
+                if (lane < kSclRows) dma16_at<slot * kSclB>(r.src, t * kRowF + kScaleOff, ls0);
             }
         } else {
             // gathered rows: each lane addresses its own row of the list
-            const int last = (v > 0 ? v : 1) - 1;
             auto rowp = [&](int t) -> const uint8_t* {
-                if (v <= 0) return kZeroRow;
-                return p.kv + int64_t(sm.rows[j0 + (t < last ? t : last)]) * kRowF;
+                if (r.v <= 0) return kZeroRow;
+                return p.kv + int64_t(sm.rows[r.j0 + (t < r.last ? t : r.last)]) * kRowF;
             };
-            static_for<0, kCodeLoads>([&](auto kc) {
-                constexpr int k = decltype(kc)::value;
+            if constexpr (kk < kCodeLoads) {
+                constexpr int k = kk;
                 const int t = 2 * (wv * kCodeLoads + k) + h;
                 dma16_v_at<slot * kCodesB + k * 1024>(rowp(t) + (c_x ^ (u_bits(k) << 4)), lc0);
-            });
-            static_for<0, kRopeLoads>([&](auto kc) {
-                constexpr int k = decltype(kc)::value;
+            } else if constexpr (kk < kCodeLoads + kRopeLoads) {
+                constexpr int k = kk - kCodeLoads;
                 const int t = 8 * (wv * kRopeLoads + k) + rr;
                 dma16_v_at<slot * kRopeSB + k * 1024>(rowp(t) + (r_x ^ ((4 * (k & 1)) << 4)) + kRopeOff, lr0);
-            });
-            if (lane < kSclRows) dma16_v_at<slot * kSclB>(rowp(s_row) + kScaleOff, ls0);
+            } else {
+                if (lane < kSclRows) dma16_v_at<slot * kSclB>(rowp(s_row) + kScaleOff, ls0);
+            }
         }
+    };
+    // all loads of sub-tile j at once (the two sub-tiles before the loop)
+    auto issue = [&](int j, auto slot_c) {
+        const SrcF r = prep(j, block_of(j), slot_c);
+        static_for<0, kLoads>([&](auto kc) { load_one(r, slot_c, kc); });
     };
     // real rows of sub-tile j (0 for padding); its scores past that are masked
     auto sub_count = [&](int j) { return max(0, min(kSub, tok1 - tok0 - j * kSub)); };
@@ -353,6 +378,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         issue(0, S0{});
         issue(1, S1{});
     }
+    int32_t blk_ahead = block_of(2);  // block id of the next dense sub-tile to load
 
     f32x16 acc[kDvTiles];
 #pragma unroll
@@ -402,7 +428,14 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         if (j + 1 < n_pad) wait_vm<kLoads>();
         else wait_vm<0>();
         __builtin_amdgcn_s_barrier();
-        if (j + 2 < n_pad) issue(j + 2, std::integral_constant<int, (sc + 2) % kRingF>{});
+        // Sub-tile j+2 goes to the slot sub-tile j-1 used.  Its loads are dealt
+        // over the output product below: issued together, the workgroup's
+        // wave-wide loads queue behind each other at the address unit and
+        // stall in-order issue.
+        using SL = std::integral_constant<int, (sc + 2) % kRingF>;
+        const bool do_load = j + 2 < n_pad;
+        SrcF ld{kZeroRow, 0, 0, 0, false};
+        if (do_load) ld = prep(j + 2, blk_ahead, SL{});
         const int cnt = bad_slot[sc] ? 0 : sub_count(j);
         bad_block |= bad_slot[sc];
         // group scales of sub-tile j, transposed to [group][token]
@@ -496,8 +529,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         l += ps;
 
         // ---- O^T += sum_g C_g^T . (P (.) scale_g)^T ----------------------------
+        // (the loads of sub-tile j+2 go out here, up to three per group)
         static_for<0, 4>([&](auto gc) {
             constexpr int g = decltype(gc)::value;
+            static_for<0, 3>([&](auto uc) {
+                constexpr int kk = 3 * g + decltype(uc)::value;
+                if constexpr (kk < kLoads) {
+                    if (do_load) load_one(ld, SL{}, std::integral_constant<int, kk>{});
+                }
+            });
             float scg[16];
             load_scales(sc, g, scg);
             bf16x8 pf[2];
@@ -520,6 +560,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
             }
             __builtin_amdgcn_sched_barrier(0);
         });
+        // every LDS read of this iteration has been consumed: the block id of
+        // the sub-tile the next iteration loads is requested now
+        blk_ahead = block_of(j + 3);
+        __builtin_amdgcn_sched_barrier(0);
     };
     for (int j = 0; j < n_pad; j += kRingF) {
         iteration(j, S0{});
@@ -536,14 +580,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     // whole row: the shard's output; a chunk of a split row: its partial slot
     const bool direct = id.slot < 0;
     const size_t orow = direct ? size_t(id.row) * p.H + head : size_t(id.slot) * p.H + head;
-    if (p.out_dtype == MLA_BF16) {
+    // chunk partials stay float32 whatever the output dtype
+    if (direct && p.out_dtype == MLA_BF16) {
         // staged through the ring's LDS once every wave is past its last read
         constexpr int kPasses = NW == 2 ? 1 : 2;
         constexpr int kWaveB = 32 * 1024 / kPasses;
         static_assert(sizeof(sm) >= NW * kWaveB, "staging fits the LDS of the ring");
         __syncthreads();
         store_rows_bf16<kPasses>(acc, inv, (MLA_LDS uint8_t*)&sm + wave * kWaveB,
-                                    static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) +
+                                    static_cast<uint16_t*>(p.o_out) +
                                         (orow - col) * kLatent,
                                     lane);
     } else {

@@ -121,10 +121,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     // ---- sub-tile loads ----------------------------------------------------
     // Wave w loads the latent parts of rows 4k + w (k = 0..7), one row per
     // wave-wide load (lane i fetches the chunk stored at position i), and the
-    // rope parts of rows 8w .. 8w + 7 in one load.  A full sub-tile uses
-    // per-lane offsets computed once; a partial one (rows at or past its
-    // valid count re-read its last valid row) and the zero row of a bad or
-    // padding sub-tile take a clamped path.
+    // rope parts of rows 8w .. 8w + 7 in one load.  Per-lane offsets are
+    // computed once; rows at or past a partial sub-tile's valid count re-read
+    // its last valid row, and a bad or padding sub-tile reads the zero row.
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     int dv[kSub / 4];  // latent loads of a full sub-tile
 #pragma unroll
@@ -134,7 +133,6 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     }
     const int r_row = 8 * wave + (lane >> 3);  // rope load: row and chunk of this lane
     const int r_off = (kLatent / 8 + ((lane & 7) ^ rswz(r_row))) << 4;
-    const int ro_full = r_row * kRowB + r_off;
     // LDS destinations: lat_row(slot, 4k + w) = w * 8 KB + (k & 3) * 32 KB +
     // (k >> 2) * 1 KB + slot * 2 KB; rope_row(slot, 8w) = rope base + slot * 4 KB + w * 1 KB
     const uint32_t lds0 = lds_addr(sm.ring);
@@ -147,24 +145,29 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         (const __attribute__((address_space(4))) int32_t*)bt;
     bool bad_slot[kRing] = {false, false, false, false};  // sub-tile in the slot had a bad block id
     // Source of sub-tile j: first row in HBM, and the last row to read (rows
-    // past it re-read it); full = a whole sub-tile of one valid block.
+    // past it re-read it).
     struct Src {
         const uint8_t* src;
         int last;
-        bool full;
     };
-    auto source = [&](int j, auto slot_c) -> Src {
+    // block id of sub-tile j (-1 for a padding sub-tile, whose table entry is
+    // not read).  The main loop reads it one iteration before its loads are
+    // issued: waiting for a scalar load right before them would stall every
+    // wave at the top of each iteration.
+    auto block_of = [&](int j) -> int32_t {
+        const uint32_t j0 = uint32_t(tok0) + uint32_t(j) * kSub;
+        return j0 < uint32_t(tok1) ? btc[j0 / kBlock] : -1;
+    };
+    auto source = [&](int j, int32_t blk, auto slot_c) -> Src {
         constexpr int slot = decltype(slot_c)::value;
         const uint32_t j0 = uint32_t(tok0) + uint32_t(j) * kSub;
         const int v = min(kSub, tok1 - int(j0));  // <= 0: padding
-        Src r{kZeroRow, 0, false};
+        Src r{kZeroRow, 0};
         bool bad = false;
         if (v > 0) {
-            const int32_t blk = btc[j0 / kBlock];
             if (blk >= 0 && blk < p.pool_blocks) {
                 r.src = p.kv + (int64_t(blk) * kBlock + (j0 % kBlock)) * kRowB;
                 r.last = v - 1;
-                r.full = v == kSub;
             } else {
                 bad = true;
             }
@@ -173,36 +176,29 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         return r;
     };
     // load k of this wave for a sub-tile in `slot`: k < 8 the latent part of
-    // row 4k + w, k = 8 the rope parts of rows 8w .. 8w + 7
+    // row 4k + w, k = 8 the rope parts of rows 8w .. 8w + 7.  Branch free:
+    // rows past r.last re-read row r.last through a row shift that is uniform
+    // over the wave for the latent loads (a scalar max) and one v_min for the
+    // rope load; a whole sub-tile shifts by 0.  (A wave issues in order, and
+    // branches and 64-bit address arithmetic around each of these loads cost
+    // more than the loads themselves.)
     auto load = [&](const Src& r, auto slot_c, auto k_c) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr int k = decltype(k_c)::value;
         if constexpr (k < kSub / 4) {
             constexpr int imm = (k & 3) * 8 * 4 * kLatB + (k >> 2) * kLatB + slot * 2 * kLatB;
-            if (r.full) {
-                dma16_at<imm>(r.src, dv[k], m_lat);
-            } else {
-                const int t = 4 * k + wv;
-                const int dt = t > r.last ? t - r.last : 0;
-                dma16_at<imm>(r.src, dv[k] - dt * kRowB, m_lat);
-            }
+            const int dt = max(4 * k + wv - r.last, 0);
+            dma16_at<imm>(r.src, dv[k] - dt * kRowB, m_lat);
         } else {
             constexpr int imm = slot * kSub * kRopeB;
-            const int ro = r.full ? ro_full : (r_row < r.last ? r_row : r.last) * kRowB + r_off;
-            dma16_at<imm>(r.src, ro, m_rope);
+            dma16_at<imm>(r.src, min(r_row, r.last) * kRowB + r_off, m_rope);
         }
     };
     // all loads of sub-tile j, issued together (one branch for the common
     // case of a whole valid sub-tile)
     auto issue = [&](int j, auto slot_c) {
-        const Src r = source(j, slot_c);
-        if (r.full) {
-            const Src f{r.src, kSub - 1, true};
-            static_for<0, kLoadsPerWave>([&](auto kc) { load(f, slot_c, kc); });
-        } else {
-            const Src c{r.src, r.last, false};
-            static_for<0, kLoadsPerWave>([&](auto kc) { load(c, slot_c, kc); });
-        }
+        const Src r = source(j, block_of(j), slot_c);
+        static_for<0, kLoadsPerWave>([&](auto kc) { load(r, slot_c, kc); });
     };
     // real rows of sub-tile j (0 for padding); its scores past that are masked
     auto sub_count = [&](int j) { return max(0, min(kSub, tok1 - tok0 - j * kSub)); };
@@ -219,6 +215,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         issue(1, S1{});
         issue(2, S2{});
     }
+    int32_t blk_ahead = block_of(kAhead);  // block id of the next sub-tile to load
 
     f32x16 acc[kDvTiles];
 #pragma unroll
@@ -277,19 +274,41 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     // LDS and are dead early), then the 32 latent steps
     auto step_ks = [](int r) { return r < 4 ? kQLatSteps + r : r - 4; };
 
-    // ---- main loop, software pipelined ---------------------------------------
+    // ---- main loop: one flat schedule of 68 MFMA slots per sub-tile ----------
     // Iteration j issues the score product of sub-tile j+1 (36 MFMAs) and the
-    // output product of sub-tile j (32 MFMAs).  The first kLead score steps
-    // carry the softmax of sub-tile j (VALU work that overlaps the matrix
-    // cores); the rest alternate with the output tiles, spreading the K and
-    // V^T reads from LDS over the iteration.  The loop is unrolled by the ring
-    // size, so every slot offset is a compile-time immediate, and scores
-    // alternate between two register sets, so a just-written MFMA result is
-    // never copied.  In the last iteration the score slot runs on whatever
-    // the next slot holds and its result is dropped.
-    constexpr int kLead = kQSteps - kDvTiles;  // 20 score steps before the first output tile
-    constexpr int kAK = 2;                     // K fragments read this many steps ahead
-    constexpr int kAV = 2;                     // V^T tiles read this many tiles ahead
+    // output product of sub-tile j (32 MFMAs: 16 output tiles x 2 token
+    // halves), with the softmax of sub-tile j spread over the slots.  A wave issues in order,
+    // and about four independent VALU instructions (or two exponentials)
+    // execute under one 32-cycle MFMA; beyond that each costs the matrix core
+    // idle cycles, so the VALU work is dealt out at that rate:
+    //   slots  0..13  score steps 0..13, with the max tree, the reference
+    //                 update and the first eight probabilities (token half 0);
+    //                 the max tree comes before the first MFMA, which waits
+    //                 for the sub-tile's first K fragments from LDS
+    //   slots 14..45  output tiles of token half 0 alternating with score
+    //                 steps 14..29, with the other eight probabilities, the
+    //                 normaliser, and the nine loads of sub-tile j+3
+    //   slots 46..67  output tiles of token half 1, with score steps 30..35
+    // The loop is unrolled by the ring size, so every slot offset is a
+    // compile-time immediate, and scores alternate between two register sets,
+    // so a just-written MFMA result is never copied.  In the last iteration
+    // the score slot runs on whatever the next slot holds and its result is
+    // dropped.
+    constexpr int kAK = 2;  // K fragments read this many score steps ahead
+    constexpr int kAV = 2;  // V^T fragments read this many output MFMAs ahead
+    constexpr int kSlots = kQSteps + 2 * kDvTiles;  // 68
+    // slot of score step r, and of output MFMA u = 16 jj + mt
+    constexpr auto qk_slot = [](int r) { return r < 14 ? r : r < 30 ? 15 + 2 * (r - 14) : 48 + 3 * (r - 30); };
+    constexpr auto pv_slot = [](int u) {
+        const int mt = u & 15;
+        return u < 16 ? 14 + 2 * mt : mt < 12 ? 46 + 3 * (mt >> 1) + (mt & 1) : 52 + mt;
+    };
+    // the probability pair p (elements 2p, 2p + 1): fma, exp2, sum + pack slots
+    constexpr auto fma_slot = [](int p) { return p < 4 ? 4 + 2 * p : 16 + 4 * (p - 4); };
+    constexpr auto exp_slot = [](int p) { return p < 4 ? 5 + 2 * p : 18 + 4 * (p - 4); };
+    constexpr auto sum_slot = [](int p) { return p < 4 ? 6 + 2 * p : 20 + 4 * (p - 4); };
+    constexpr int kSumSlot = 34;                        // normaliser
+    constexpr auto load_slot = [](int k) { return 15 + 3 * k; };  // the nine loads of sub-tile j+3
 
     f32x16 sA, sB;
     if (n_pad > 0) {
@@ -316,14 +335,20 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         if (j + 2 < n_pad) wait_vm<kLoadsPerWave>();
         else wait_vm<0>();
         __builtin_amdgcn_s_barrier();
-        // sub-tile j+3 goes to the slot sub-tile j-1 used
-        if (j + kAhead < n_pad) issue(j + kAhead, std::integral_constant<int, (sc + kAhead) % kRing>{});
+        // sub-tile j+3 goes to the slot sub-tile j-1 used.  Its source comes
+        // from the block id read at the end of the last iteration (no LDS
+        // read is in flight here, so waiting for it waits for nothing else).
+        // Past the last sub-tile the loads still go out, reading the zero
+        // row into that free slot (no sub-tile uses it again), so the issue
+        // path has no branch.
+        using SL = std::integral_constant<int, (sc + kAhead) % kRing>;
+        const Src ld = j + kAhead < n_pad ? source(j + kAhead, blk_ahead, SL{}) : Src{kZeroRow, 0};
         // a bad block id's sub-tile holds zero rows: all its scores are
         // masked below; no early exit
         const int cnt = bad_slot[sc] ? 0 : sub_count(j);
         bad_block |= bad_slot[sc];
 
-        // K (and rope Q) fragments are read kAK steps ahead of their MFMA
+        // K (and rope Q) fragments of sub-tile j+1, kAK score steps ahead
         bf16x8 kf[kAK + 1];
         bf16x8 qrf[kAK + 1];
 #pragma unroll
@@ -341,16 +366,26 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
             if (r == 0) mfma32_v_first(nxt, a, b);
             else mfma32_v(nxt, a, b);
         };
-
-        // ---- phase 1: score steps 0 .. kLead-1 with the softmax of sub-tile j
-        // (log2 domain; the reference max m may lag the running max by kLag)
-        float mx = 0.f, nm = 0.f, ps = 0.f;
+        // V^T fragments of sub-tile j, kAV output MFMAs ahead; probabilities
+        // of token half jj in pf[jj]
+        bf16x8 vf[kAV + 1];
         bf16x8 pf[2];
-        bf16x8 vf[kAV + 1][2];
-        static_for<0, kLead>([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            qk_step(r);
-            if (r == 0) {
+        auto pv_step = [&](int u, bool fresh) {
+            if (u + kAV < 2 * kDvTiles) vf[(u + kAV) % (kAV + 1)] = vread(sc, (u + kAV) >> 4, (u + kAV) & 15);
+            const int mt = u & 15;
+            if (fresh) mfma32_acc<true>(acc[mt], vf[u % (kAV + 1)], pf[u >> 4]);
+            else mfma32_acc(acc[mt], vf[u % (kAV + 1)], pf[u >> 4]);
+        };
+
+        // softmax of sub-tile j (log2 domain; the reference max m may lag the
+        // running max by kLag): the max is a depth-3 tree of max3, and each
+        // probability pair goes through fma, exp2 and sum + pack in three
+        // different slots, so no VALU instruction waits on the one before it
+        float mt3[5], mu[2];
+        float mx = 0.f, nm = 0.f, ps0 = 0.f, ps1 = 0.f;
+        static_for<0, kSlots>([&](auto sc_) {
+            constexpr int s = decltype(sc_)::value;
+            if constexpr (s == 0) {
                 // only a partial or masked sub-tile needs masking
                 if (cnt < kSub) {
 #pragma unroll
@@ -359,13 +394,15 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
                         if (tok >= cnt) cur[i] = -INFINITY;
                     }
                 }
-                mx = fmaxf(fmaxf(cur[0], cur[1]), cur[2]);
 #pragma unroll
-                for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, cur[i]), cur[i + 1]);
-                mx = fmaxf(mx, cur[15]);
-            } else if (r == 1) {
+                for (int k = 0; k < 5; ++k) mt3[k] = fmaxf(fmaxf(cur[3 * k], cur[3 * k + 1]), cur[3 * k + 2]);
+            } else if constexpr (s == 1) {
+                mu[0] = fmaxf(fmaxf(mt3[0], mt3[1]), mt3[2]);
+                mu[1] = fmaxf(fmaxf(mt3[3], mt3[4]), cur[15]);
+                mx = fmaxf(mu[0], mu[1]);
+            } else if constexpr (s == 2) {
                 mx = xhalf_max(mx) * sl2;
-            } else if (r == 2) {
+            } else if constexpr (s == 3) {
                 // raw scores are scaled inside the exponent (scale > 0 keeps
                 // the order).  A head whose max grew by more than kLag moves
                 // its reference; accumulators of heads that had one rescale.
@@ -379,43 +416,47 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
                 if (grow) m = mx;
                 // with no valid score yet (m = -inf) every term is 0
                 nm = (m == -INFINITY) ? 0.f : -m;
-            } else if (r >= 3 && r < 19) {
-                const int i = r - 3;
-                const float e = __builtin_amdgcn_exp2f(fmaf(cur[i], sl2, nm));
-                cur[i] = e;
-                ps += e;
-            } else if (r == 19) {
-                ps = xhalf_sum(ps);
-                l += ps;
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pf[jj][e] = (__bf16)cur[8 * jj + e];
             }
-            if (r == kLead - 2) {
-                vf[0][0] = vread(sc, 0, 0);
-                vf[0][1] = vread(sc, 1, 0);
-            } else if (r == kLead - 1) {
-                vf[1][0] = vread(sc, 0, 1);
-                vf[1][1] = vread(sc, 1, 1);
-            }
+            static_for<0, 8>([&](auto pc) {
+                constexpr int pp = decltype(pc)::value;
+                constexpr int i = 2 * pp;
+                if constexpr (s == fma_slot(pp)) {
+                    cur[i] = fmaf(cur[i], sl2, nm);
+                    cur[i + 1] = fmaf(cur[i + 1], sl2, nm);
+                } else if constexpr (s == exp_slot(pp)) {
+                    cur[i] = __builtin_amdgcn_exp2f(cur[i]);
+                    cur[i + 1] = __builtin_amdgcn_exp2f(cur[i + 1]);
+                } else if constexpr (s == sum_slot(pp)) {
+                    ps0 += cur[i];
+                    ps1 += cur[i + 1];
+                    pf[i >> 3][i & 7] = (__bf16)cur[i];
+                    pf[i >> 3][(i & 7) + 1] = (__bf16)cur[i + 1];
+                }
+            });
+            if constexpr (s == kSumSlot) l += xhalf_sum(ps0 + ps1);
+            // the first two V^T fragments, two slots before the first output MFMA
+            if constexpr (s == pv_slot(0) - 2) vf[0] = vread(sc, 0, 0);
+            if constexpr (s == pv_slot(0) - 1) vf[1] = vread(sc, 0, 1);
+            static_for<0, kLoadsPerWave>([&](auto kc) {
+                if constexpr (s == load_slot(decltype(kc)::value)) load(ld, SL{}, kc);
+            });
+            // the slot's MFMA
+            static_for<0, kQSteps>([&](auto rc) {
+                if constexpr (qk_slot(decltype(rc)::value) == s) qk_step(decltype(rc)::value);
+            });
+            static_for<0, 2 * kDvTiles>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                // the first output MFMA reads probabilities packed by VALU
+                // converts just before: it leads with the two wait states
+                if constexpr (pv_slot(u) == s) pv_step(u, u == 0 || u == kDvTiles);
+            });
             __builtin_amdgcn_sched_barrier(0);
         });
-
-        // ---- phase 2: O^T += V^T . P^T, one output tile per remaining score step
-#pragma unroll
-        for (int mt = 0; mt < kDvTiles; ++mt) {
-            if (mt + kAV < kDvTiles) {
-                vf[(mt + kAV) % (kAV + 1)][0] = vread(sc, 0, mt + kAV);
-                vf[(mt + kAV) % (kAV + 1)][1] = vread(sc, 1, mt + kAV);
-            }
-            const int v = mt % (kAV + 1);
-            if (mt == 0) mfma32_acc<true>(acc[mt], vf[v][0], pf[0]);
-            else mfma32_acc(acc[mt], vf[v][0], pf[0]);
-            mfma32_acc(acc[mt], vf[v][1], pf[1]);
-            qk_step(kLead + mt);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        // Every LDS read of this iteration has been consumed: a scalar load
+        // issued now is waited for only by the next iteration's source, after
+        // its barrier.
+        blk_ahead = block_of(j + kAhead + 1);
+        __builtin_amdgcn_sched_barrier(0);
         // wait states before the next iteration's VALU reads the scores just
         // accumulated (the compiler does not see the asm as an MFMA)
         asm volatile("s_nop 7\n\ts_nop 3");
@@ -427,6 +468,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         iteration(j + 3, S3{}, sB, sA);
     }
     mfma_drain();
+    wait_vm<0>();  // the zero-row loads of the last iterations land before the staging below
     if (bad_block && threadIdx.x == 0) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
 
     // ---- finalise: O = acc / l, LSE = ln 2 * (m + log2 l) --------------------
@@ -436,12 +478,13 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     // whole row: the shard's output; a chunk of a split row: its partial slot
     const bool direct = id.slot < 0;
     const size_t orow = direct ? size_t(id.row) * p.H + head : size_t(id.slot) * p.H + head;
-    if (p.out_dtype == MLA_BF16) {
+    // chunk partials stay float32 whatever the output dtype
+    if (direct && p.out_dtype == MLA_BF16) {
         // staged through the ring's LDS once every wave is past its last read
         static_assert(sizeof(sm) >= 4 * 32 * 1024, "staging fits the LDS of the ring");
         __syncthreads();
         store_rows_bf16<1>(acc, inv, (MLA_LDS uint8_t*)&sm + wave * 32 * 1024,
-                            static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) + (orow - col) * kLatent,
+                            static_cast<uint16_t*>(p.o_out) + (orow - col) * kLatent,
                             lane);
     } else {
         float* o = static_cast<float*>(direct ? p.o_out : p.ws_o) + orow * kLatent;

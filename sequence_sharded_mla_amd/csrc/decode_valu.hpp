@@ -225,12 +225,13 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams p) {
     // whole row: the shard's output; a chunk of a split row: its partial slot
     const bool direct = id.slot < 0;
     const size_t head = (direct ? size_t(id.row) : size_t(id.slot)) * p.H + h0 + h;
-    if (p.out_dtype == MLA_F32) {
+    // chunk partials stay float32 whatever the output dtype
+    if (p.out_dtype == MLA_F32 || !direct) {
         float* o = static_cast<float*>(direct ? p.o_out : p.ws_o) + head * kLatent;
 #pragma unroll
         for (int i = 0; i < 32; ++i) o[tl + 16 * i] = acc[i] * inv;
     } else {
-        uint16_t* o = static_cast<uint16_t*>(direct ? p.o_out : p.ws_o) + head * kLatent;
+        uint16_t* o = static_cast<uint16_t*>(p.o_out) + head * kLatent;
 #pragma unroll
         for (int i = 0; i < 32; ++i) o[tl + 16 * i] = uint16_t(bf16x2_rne(acc[i] * inv, 0.f));
     }

@@ -54,7 +54,33 @@ static int32_t plan_target(const mla_decode_desc* d) {
     return 512;
 }
 
-int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan, int32_t n_q) {
+// Item, row and partial-slot bounds of a planned step with p->target items
+// (and the workspace offsets after `off`); returns the workspace end.
+static int64_t size_planned(const mla_decode_desc* d, Plan* p, int64_t off) {
+    // items per row <= local / chunk + 1 and sum(local) / chunk <= target
+    p->items_max = p->rows + p->target;
+    // a row splits only when local > chunk >= chunk_min, into at most
+    // 2 local / chunk items: at most 2 target and 2 total / chunk_min
+    const int64_t total_bound = int64_t(p->rows) * d->max_blocks * kBlock;
+    int64_t slots = 2 * int64_t(p->target);
+    const int64_t by_len = 2 * ((total_bound + p->chunk_min - 1) / p->chunk_min);
+    if (by_len < slots) slots = by_len;
+    if (p->items_max < slots) slots = p->items_max;
+    p->slots = int32_t(slots);
+    p->items_off = off;
+    off = align_up(off + int64_t(p->items_max) * 16, 256);
+    p->row_info_off = off;
+    off = align_up(off + int64_t(p->rows) * 8, 256);
+    p->ws_o_off = off;
+    off = align_up(off + slots * d->num_heads * kLatent * 4, 256);  // float32 partials
+    p->ws_lse_off = off;
+    off = align_up(off + slots * d->num_heads * 4, 256);
+    return off;
+}
+
+static int64_t planned_bytes(const mla_decode_desc* d, Plan p, int64_t off) { return size_planned(d, &p, off); }
+
+int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan, int32_t n_q, int64_t ws_cap) {
     int32_t st = validate_desc(d);
     if (st != MLA_OK) return st;
     if (shard_count < 1 || shard_count > 4096) return MLA_ERR_SHARD;
@@ -80,27 +106,13 @@ int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan, int
     off = align_up(off + int64_t(n_q) * 16, 256);
     if (p.planned) {
         p.target = few_rows ? plan_target(d) / 2 : plan_target(d);
-        // items per row <= local / chunk + 1 and sum(local) / chunk <= target
-        p.items_max = p.rows + p.target;
-        // a row splits only when local > chunk >= chunk_min, into at most
-        // 2 local / chunk items: at most 2 target and 2 total / chunk_min
-        const int64_t total_bound = int64_t(p.rows) * d->max_blocks * kBlock;
-        int64_t slots = 2 * int64_t(p.target);
-        const int64_t by_len = 2 * ((total_bound + p.chunk_min - 1) / p.chunk_min);
-        if (by_len < slots) slots = by_len;
-        if (p.items_max < slots) slots = p.items_max;
-        p.slots = int32_t(slots);
-        const int64_t out_bytes = d->out_dtype == MLA_F32 ? 4 : 2;
-        p.items_off = off;
-        off = align_up(off + int64_t(p.items_max) * 16, 256);
-        p.row_info_off = off;
-        off = align_up(off + int64_t(p.rows) * 8, 256);
-        p.ws_o_off = off;
-        off = align_up(off + slots * d->num_heads * kLatent * out_bytes, 256);
-        p.ws_lse_off = off;
-        off = align_up(off + slots * d->num_heads * 4, 256);
+        // a capped workspace plans fewer, longer chunks until the partials fit
+        if (ws_cap > 0)
+            while (p.target > 1 && planned_bytes(d, p, off) > ws_cap) p.target /= 2;
+        off = size_planned(d, &p, off);
     }
     p.ws_bytes = off;
+    if (ws_cap > 0 && p.ws_bytes > ws_cap) return MLA_ERR_WORKSPACE;
     *plan = p;
     return MLA_OK;
 }

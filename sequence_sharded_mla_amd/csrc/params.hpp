@@ -16,7 +16,7 @@ struct DecodeParams {
                                  // null: Tq tokens per request
     void* o_out;                 // [shard_count][n_q][H][512] out dtype
     float* lse_out;              // [shard_count][n_q][H]
-    void* ws_o;                  // partials of split rows: [slots][H][512] out dtype
+    float* ws_o;                 // partials of split rows: [slots][H][512] float32
     float* ws_lse;               // [slots][H]
     const int32_t* items;        // [n][4] row, chunk, partial slot (-1: whole row), 0;
                                  // null: one item per row, covering all of it

@@ -44,7 +44,7 @@ struct Plan {
     int64_t qmap_off = 0;       // int32 [n_q][4]
     int64_t items_off = 0;      // int32 [items_max][4]
     int64_t row_info_off = 0;   // int32 [rows][2]
-    int64_t ws_o_off = 0;       // out dtype [slots][H][512]
+    int64_t ws_o_off = 0;       // float [slots][H][512]
     int64_t ws_lse_off = 0;     // float [slots][H]
 };
 
@@ -55,7 +55,11 @@ int32_t local_len(int32_t context_len, int32_t shard_id, int32_t n_shards);
 // the status code of the first failed check.
 int32_t validate_desc(const mla_decode_desc* d);
 // n_q: query tokens per shard, at most batch * q_len (-1: batch * q_len).
-int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan, int32_t n_q = -1);
+// ws_cap > 0: the workspace may not exceed ws_cap bytes; a planned step then
+// aims for fewer, longer chunks until its partials fit, and the call fails
+// with MLA_ERR_WORKSPACE when even that does not fit.
+int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan, int32_t n_q = -1,
+                  int64_t ws_cap = -1);
 
 bool aligned16(const void* p);
 

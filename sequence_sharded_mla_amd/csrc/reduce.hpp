@@ -243,10 +243,7 @@ __global__ void __launch_bounds__(256) chunk_combine_kernel(DecodeParams p, int 
     const int32_t slot0 = p.row_info[2 * size_t(row)];  // a row's slots are consecutive
     const int32_t k = p.row_info[2 * size_t(row) + 1];
     if (k <= 1) return;
-    if (p.out_dtype == MLA_F32)
-        combine_heads<float>(p, row, slot0, k, hpw);
-    else
-        combine_heads<uint16_t>(p, row, slot0, k, hpw);
+    combine_heads<float>(p, row, slot0, k, hpw);  // partials are float32
 }
 
 constexpr int kPlanThreads = 256;

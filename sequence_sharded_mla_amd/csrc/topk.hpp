@@ -43,7 +43,11 @@ constexpr int kBins = 4096;       // 12-bit digits
 constexpr int kCand = 2048;       // tied group resolved in LDS (a power of two)
 constexpr int kSel = 2048;        // local rows with K <= kSel list their selection in LDS
 constexpr int kMaxMergeK = 8192;  // output list sorted in LDS by the merge
-constexpr int64_t kMaxLocal = int64_t(1) << 19;   // local positions per row (64 KB bitmap in LDS)
+// Local positions per row: the row's bitmap (32 positions in two 32-bit
+// words: bits and a running count) is 8 B per 32 positions of dynamic LDS
+// beside the kernel's static state (about 58 KB), inside the 160 KB a
+// workgroup may hold.
+constexpr int64_t kMaxLocal = 393216;
 constexpr int64_t kMaxCand = int64_t(1) << 18;    // candidates per merged row (32 KB bitmap)
 constexpr int kStage = 32768;     // merge rows of up to kStage / 2 candidates are read once into LDS
 constexpr int kStageK = kCand;    // largest K the staged merge sorts in the tied-group space
@@ -573,6 +577,8 @@ __device__ bool varlen_token(const int32_t* qsl, int32_t B, int32_t n_q, int32_t
 // bitmap (one bit per local position of the longest row of the launch) and
 // the running count of set bits before each bitmap word.
 // Two workgroups per CU (LDS allows it): at most 128 VGPRs.
+static_assert(sizeof(SelectShared) + sizeof(SelList) + kMaxLocal / 32 * 8 + 1024 <= 160 * 1024,
+              "the longest local row's bitmap fits beside the selection's static LDS");
 __global__ void __launch_bounds__(kThreads, 4) local_topk_kernel(LocalParams p, int32_t bitmap_words) {
     __shared__ SelectShared sh;
     __shared__ SelList sel;

@@ -331,7 +331,9 @@ def test_topk_checks(lib):
                                   None if ws is None else v(ws), None)
 
     assert loc(stride=0) == _lib.MLA_ERR_SHAPE
-    assert loc(stride=(1 << 19) + 1) == _lib.MLA_ERR_SHAPE
+    # the longest row whose position bitmap fits in LDS beside the selection state
+    assert loc(stride=393216 + 1) == _lib.MLA_ERR_SHAPE
+    assert loc(stride=1 << 19) == _lib.MLA_ERR_SHAPE
     assert loc(k=0) == _lib.MLA_ERR_SHAPE
     assert loc(Tq=0) == _lib.MLA_ERR_SHAPE
     assert loc(B=-1) == _lib.MLA_ERR_SHAPE

@@ -273,3 +273,12 @@ def test_varlen_offsets_not_a_partition_raise_the_error_word():
         torch.cuda.synchronize()
         assert mla_get_device_error(ws) & MLA_DEVERR_QUERY, bad
         assert torch.all(ci == -1) and torch.all(torch.isneginf(cs)), bad
+
+
+def test_longest_supported_local_row():
+    """A shard row at the longest supported stride (393,216 positions, the
+    largest whose position bitmap fits in LDS beside the selection state)."""
+    say("topk longest row")
+    L = 393216
+    scores = workload.indexer_scores(1, 1, L, seed=77)
+    check_selection(scores, np.array([L]), 1, 2048, 1)
