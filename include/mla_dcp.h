@@ -160,6 +160,27 @@ int32_t mla_decode_partial(const mla_decode_desc* desc, const void* q, const voi
                            void* o_partial, float* lse, void* workspace,
                            int64_t workspace_bytes, void* stream);
 
+/* mla_decode_partial for callers that cannot allocate or pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * device allocation.  Instead of a workspace the call uses a scratch array
+ * the library holds on each GPU (64 MiB, allocated with the library's code
+ * object on that device and kept until the process ends; its address is
+ * looked up once per device).  Nothing is allocated inside the call.
+ * Same inputs, outputs, checks and results as mla_decode_partial, except:
+ *   err_word   device pointer to a 32-bit word that receives the device
+ *              error bits (ORed in, never cleared by the call; read it with
+ *              mla_get_device_error(err_word, ...)), or NULL to drop them
+ * A call whose chunk plan and partials would not fit in the scratch plans
+ * fewer, longer chunks; if even that does not fit it returns
+ * MLA_ERR_WORKSPACE (a call of more than about a million query tokens).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (different streams or threads without ordering between them) race and
+ * give undefined results; calls ordered on one stream are fine. */
+int32_t mla_decode_partial_noalloc(const mla_decode_desc* desc, const void* q, const void* kv_pool,
+                                   const int32_t* block_table, const int32_t* context_lens,
+                                   const int32_t* topk_idx, int32_t shard_id, int32_t n_shards,
+                                   void* o_partial, float* lse, uint32_t* err_word, void* stream);
+
 /* The same for shards shard_begin .. shard_begin + shard_count - 1 of
  * n_shards in one launch (all shards of one cache emulated on one GPU).
  *   block_tables [shard_count][B][max_blocks]

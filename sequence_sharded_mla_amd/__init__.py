@@ -96,6 +96,17 @@ def mla_decode_partial(desc, q, kv_pool, block_table, context_lens, topk_idx, sh
         workspace.numel(), _stream(stream)), "mla_decode_partial")
 
 
+def mla_decode_partial_noalloc(desc, q, kv_pool, block_table, context_lens, topk_idx, shard_id,
+                               n_shards, o_partial, lse, err_word=None, stream=None):
+    """mla_decode_partial with the library's own per-device scratch instead of
+    a workspace (no allocation inside the call); err_word: a device int32 /
+    uint32 tensor receiving the device error bits, or None."""
+    _check(_lib.load().mla_decode_partial_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(kv_pool), _ptr(block_table), _ptr(context_lens),
+        _ptr(topk_idx), shard_id, n_shards, _ptr(o_partial), _ptr(lse), _ptr(err_word),
+        _stream(stream)), "mla_decode_partial_noalloc")
+
+
 def mla_decode_partial_shards(desc, q, kv_pool, block_tables, context_lens, topk_idx,
                               shard_begin, shard_count, n_shards, o_partials, lses, workspace,
                               stream=None):

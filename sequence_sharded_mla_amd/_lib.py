@@ -61,6 +61,8 @@ SIGNATURES = {
     "mla_decode_workspace_size": (_i32, [_pdesc, _i32, ctypes.POINTER(_i64)]),
     "mla_decode_partial": (_i32, [_pdesc, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
                                   _i64, _vp]),
+    "mla_decode_partial_noalloc": (_i32, [_pdesc, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
+                                          _vp]),
     "mla_decode_partial_shards": (_i32, [_pdesc, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
                                          _vp, _vp, _i64, _vp]),
     "mla_decode_partial_shards_varlen": (_i32, [_pdesc, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,

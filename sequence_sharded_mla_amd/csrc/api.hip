@@ -1,6 +1,9 @@
 // extern "C" entry points of libmla_dcp: argument checks, plan, launches.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/mla_dcp.h"
 #include "common.hpp"
 #include "decode_fp8.hpp"
@@ -141,6 +144,34 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
 }
 
 
+// ---- scratch of the allocation-free decode call ---------------------------
+// A file-scope device array, one copy per GPU, allocated with the code object
+// and held until the process ends.  In host code its name is a host-side
+// stand-in, never a device address: the address used everywhere is the one
+// hipGetSymbolAddress returns, looked up once per device (with that device
+// current) on the call's first use of the device.
+constexpr int64_t kNoAllocScratchBytes = int64_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int32_t scratch_ptr(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_DEVICE;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MLA_OK;
+}
+
 int32_t make_slot_params(const int32_t* req_idx, const int32_t* positions, int64_t n_tokens,
                          const int32_t* block_tables, int32_t batch, int32_t max_blocks,
                          int64_t pool_blocks, int32_t shard_begin, int32_t shard_count, int32_t n_shards,
@@ -236,6 +267,23 @@ int32_t mla_decode_partial(const mla_decode_desc* desc, const void* q, const voi
     }
     return mla::decode_impl(desc, q, kv_pool, block_table, context_lens, topk_idx, shard_id, 1,
                             n_shards, o_partial, lse, workspace, workspace_bytes, stream);
+}
+
+int32_t mla_decode_partial_noalloc(const mla_decode_desc* desc, const void* q, const void* kv_pool,
+                                   const int32_t* block_table, const int32_t* context_lens,
+                                   const int32_t* topk_idx, int32_t shard_id, int32_t n_shards,
+                                   void* o_partial, float* lse, uint32_t* err_word, void* stream) {
+    if (n_shards < 1 || shard_id < 0 || shard_id >= n_shards) {
+        if (!desc) return MLA_ERR_NULL;
+        int32_t st = mla::validate_desc(desc);
+        return st != MLA_OK ? st : MLA_ERR_SHARD;
+    }
+    void* ws = nullptr;
+    int32_t st = mla::scratch_ptr(&ws);
+    if (st != MLA_OK) return st;
+    return mla::decode_impl(desc, q, kv_pool, block_table, context_lens, topk_idx, shard_id, 1, n_shards,
+                            o_partial, lse, ws, mla::kNoAllocScratchBytes, stream, nullptr, -1,
+                            mla::kNoAllocScratchBytes, err_word);
 }
 
 int32_t mla_decode_partial_shards(const mla_decode_desc* desc, const void* q,
