@@ -261,10 +261,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     auto u_bits = [](int i) { return ((2 * (i & 1)) << 2) | (((i >> 2) & 1) << 1) | ((i >> 1) & 1); };
     const int h = lane >> 5;
     const int c_x0 = ((((lane & 16) | ((lane & 15) ^ (h << 2)))) ^ u_bits(wave * kCodeLoads)) << 4;
-    const int c_h0 = (h + 2 * wave * kCodeLoads) * kRowF;
     const int rr = lane >> 3;
     const int r_x0 = (((lane & 7) ^ (rr >> 1)) ^ (4 * ((wave * kRopeLoads) & 1))) << 4;
-    const int r_h0 = (rr + 8 * wave * kRopeLoads) * kRowF + kRopeOff;
     const int s_row0 = wave * kSclRows + lane;  // scale load (lanes < kSclRows)
     const uint32_t lc0 = __builtin_amdgcn_readfirstlane(lds_addr(sm.codes) + wv * kCodeLoads * 1024);
     const uint32_t lr0 = __builtin_amdgcn_readfirstlane(lds_addr(sm.rope) + wv * kRopeLoads * 1024);
@@ -279,7 +277,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         int32_t j0;
         int last;
         int v;  // real rows (<= 0: padding)
-        bool full;
     };
     // block id of dense sub-tile j (-1 past the range, whose entry is not
     // read).  The main loop reads it one iteration ahead, at a point where no
@@ -292,7 +289,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         constexpr int slot = decltype(slot_c)::value;
         const int32_t j0 = tok0 + j * kSub;
         const int v = min(kSub, tok1 - j0);  // <= 0: padding
-        SrcF r{kZeroRow, j0, (v > 0 ? v : 1) - 1, v, false};
+        SrcF r{kZeroRow, j0, (v > 0 ? v : 1) - 1, v};
         if (!SPARSE) {
             bool bad = false;
             r.last = 0;
@@ -300,7 +297,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
                 if (blk >= 0 && blk < p.pool_blocks) {
                     r.src = p.kv + (int64_t(blk) * kBlock + (uint32_t(j0) % kBlock)) * kRowF;
                     r.last = v - 1;
-                    r.full = v == kSub;
                 } else {
                     bad = true;
                 }
@@ -316,32 +312,23 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         constexpr int kk = decltype(kk_c)::value;
         // opaque copies: the per-load offsets below are then computed here,
         // not hoisted out of the loop into a dozen live registers
-        int c_x = c_x0, c_h = c_h0, r_x = r_x0, r_h = r_h0, s_row = s_row0;
-        asm volatile("" : "+v"(c_x), "+v"(c_h), "+v"(r_x), "+v"(r_h), "+v"(s_row));
+        int c_x = c_x0, r_x = r_x0, s_row = s_row0;
+        asm volatile("" : "+v"(c_x), "+v"(r_x), "+v"(s_row));
         if constexpr (!SPARSE) {
+            // branch free: rows past r.last re-read row r.last (one v_min per
+            // load; a whole sub-tile has r.last = 31 and clamps nothing)
             if constexpr (kk < kCodeLoads) {
                 constexpr int k = kk;
-                if (r.full) {
-                    dma16_at<slot * kCodesB + k * 1024>(r.src, (c_x ^ (u_bits(k) << 4)) + c_h + 2 * k * kRowF,
-                                                        lc0);
-                } else {
-                    const int t = 2 * (wv * kCodeLoads + k) + h;
-                    dma16_at<slot * kCodesB + k * 1024>(
-                        r.src, (c_x ^ (u_bits(k) << 4)) + (t < r.last ? t : r.last) * kRowF, lc0);
-                }
+                const int t = 2 * (wv * kCodeLoads + k) + h;
+                dma16_at<slot * kCodesB + k * 1024>(r.src, (c_x ^ (u_bits(k) << 4)) + min(t, r.last) * kRowF,
+                                                    lc0);
             } else if constexpr (kk < kCodeLoads + kRopeLoads) {
                 constexpr int k = kk - kCodeLoads;
-                if (r.full) {
-                    dma16_at<slot * kRopeSB + k * 1024>(r.src, (r_x ^ ((4 * (k & 1)) << 4)) + r_h + 8 * k * kRowF,
-                                                        lr0);
-                } else {
-                    const int t = 8 * (wv * kRopeLoads + k) + rr;
-                    dma16_at<slot * kRopeSB + k * 1024>(
-                        r.src, (r_x ^ ((4 * (k & 1)) << 4)) + kRopeOff + (t < r.last ? t : r.last) * kRowF, lr0);
-                }
+                const int t = 8 * (wv * kRopeLoads + k) + rr;
+                dma16_at<slot * kRopeSB + k * 1024>(
+                    r.src, (r_x ^ ((4 * (k & 1)) << 4)) + kRopeOff + min(t, r.last) * kRowF, lr0);
             } else {
-                const int t = (r.full || s_row < r.last) ? s_row : r.last;
-                if (lane < kSclRows) dma16_at<slot * kSclB>(r.src, t * kRowF + kScaleOff, ls0);
+                if (lane < kSclRows) dma16_at<slot * kSclB>(r.src, min(s_row, r.last) * kRowF + kScaleOff, ls0);
             }
         } else {
             // gathered rows: each lane addresses its own row of the list
@@ -432,10 +419,12 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         // over the output product below: issued together, the workgroup's
         // wave-wide loads queue behind each other at the address unit and
         // stall in-order issue.
+        // A dense step issues them past the last sub-tile too, reading the
+        // zero row into that free slot (no sub-tile reads it again), so the
+        // issue path has no branch.
         using SL = std::integral_constant<int, (sc + 2) % kRingF>;
-        const bool do_load = j + 2 < n_pad;
-        SrcF ld{kZeroRow, 0, 0, 0, false};
-        if (do_load) ld = prep(j + 2, blk_ahead, SL{});
+        const bool do_load = !SPARSE || j + 2 < n_pad;
+        const SrcF ld = j + 2 < n_pad ? prep(j + 2, blk_ahead, SL{}) : SrcF{kZeroRow, 0, 0, 0};
         const int cnt = bad_slot[sc] ? 0 : sub_count(j);
         bad_block |= bad_slot[sc];
         // group scales of sub-tile j, transposed to [group][token]
@@ -535,7 +524,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
             static_for<0, 3>([&](auto uc) {
                 constexpr int kk = 3 * g + decltype(uc)::value;
                 if constexpr (kk < kLoads) {
-                    if (do_load) load_one(ld, SL{}, std::integral_constant<int, kk>{});
+                    if (SPARSE) {
+                        if (do_load) load_one(ld, SL{}, std::integral_constant<int, kk>{});
+                    } else {
+                        load_one(ld, SL{}, std::integral_constant<int, kk>{});
+                    }
                 }
             });
             float scg[16];
@@ -571,6 +564,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         iteration(j + 2, S2{});
     }
     mfma_drain();
+    wait_vm<0>();  // the zero-row loads of the last iterations land before the staging below
     if (bad_block && threadIdx.x == 0) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
 
     // ---- finalise: O = acc / l, LSE = ln 2 * (m + log2 l) --------------------
