@@ -378,37 +378,27 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     // per-lane operand addresses inside slot 0 (plus compile-time offsets)
     const MLA_LDS uint8_t* lds_codes = (const MLA_LDS uint8_t*)sm.codes;
     const MLA_LDS uint8_t* lds_rope = (const MLA_LDS uint8_t*)sm.rope;
-    int kb[8];  // code pair s (chunk 2 s + half): kb[s & 7] + 256 (s >> 3)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) kb[u] = col * kLatent + (((2 * u + half) ^ f8swz(col)) << 4);
-    int kr[4];  // rope chunk 2 u + half
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kr[u] = col * kRope * 2 + (((2 * u + half) ^ rope_swz(col)) << 4);
-    int vb[2][4];  // V^T reads of tile mt = 4 g + q: vb[g & 1][q] + 256 (g >> 1) + 8 KB jj
+    // Per-lane LDS byte offsets of the operand reads.  The swizzled chunk
+    // index sits in bits 4-7 (bits 4-6 for rope) above a row base whose low
+    // bits are zero, so every read of a lane is its first read's offset
+    // XORed with a constant: code pair s at kb0 ^ 32 (s & 7), plus 256 (s >> 3);
+    // rope chunk 2 u + half at kr0 ^ 32 u; V^T tile 4 g + q at
+    // vb0 ^ (128 (g & 1) + 32 q), plus 256 (g >> 1) and 8 KB per token half.
+    // One base register each instead of a table of 20.
+    int kb0 = col * kLatent + ((half ^ f8swz(col)) << 4);
+    int kr0 = col * kRope * 2 + ((half ^ rope_swz(col)) << 4);
+    int vb0;
     {
         const int g16 = lane >> 4, s16 = lane & 15;
         const int r = s16 >> 1, b = s16 & 1;
         const int t = 8 * (r >> 2) + 4 * (g16 >> 1) + (r & 3);
-#pragma unroll
-        for (int g1 = 0; g1 < 2; ++g1)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                vb[g1][q] = t * kLatent + (((8 * g1 + 2 * q + (g16 & 1)) ^ f8swz(t)) << 4) + 8 * b;
+        vb0 = t * kLatent + (((g16 & 1) ^ f8swz(t)) << 4) + 8 * b;
     }
-    // scales of the 16 tokens this lane holds in S^T, tokens
-    // (i >> 2) * 8 + 4 half + (i & 3), for group g of the sub-tile in `slot`
-    auto load_scales = [&](int slot, int g, float (&sc)[16]) {
-        const MLA_LDS float* rowp =
-            (const MLA_LDS float*)((const MLA_LDS uint8_t*)&sm.sct[slot][g][0] + 16 * half);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 v = *(const MLA_LDS f32x4*)(rowp + 8 * q);
-            sc[4 * q] = v[0]; sc[4 * q + 1] = v[1]; sc[4 * q + 2] = v[2]; sc[4 * q + 3] = v[3];
-        }
-    };
-
     auto iteration = [&](int j, auto slot_c) {
         constexpr int sc = decltype(slot_c)::value;  // slot of sub-tile j
+        // opaque per iteration: the XORed offsets are formed next to their
+        // reads instead of being hoisted into live registers
+        asm volatile("" : "+v"(kb0), "+v"(kr0), "+v"(vb0));
         // own loads of sub-tile j are complete once at most one later
         // sub-tile (j+1) remains in flight; the barrier makes all waves'
         // loads visible and frees the slot of sub-tile j-1 for j+2
@@ -437,51 +427,79 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         }
 
         // ---- scores ------------------------------------------------------------
+        // A flat schedule of 36 MFMAs: 4 rope steps into st, then 32 latent
+        // steps L (group g = L / 8, code pair L / 2) into the group
+        // accumulator ag[g & 1].  Around each MFMA go, after it in program
+        // order so that they execute under it: the widening of the next
+        // step's codes (4 converts), the code read of the pair two ahead,
+        // and, during group g, the 16 scale FMAs of group g - 1 (the two
+        // accumulators alternate, so the matrix core never waits for them).
+        // A group's scales are read from LDS seven steps before their FMAs:
+        // a read consumed one step after issue stalls in-order issue for
+        // the LDS latency.
         const MLA_LDS uint8_t* lc = lds_codes + sc * kCodesB;
-        f32x16 st;
-        {
-            const MLA_LDS uint8_t* lr = lds_rope + sc * kRopeSB;
-            bf16x8 k0 = *(const MLA_LDS bf16x8*)(lr + kr[0]);
-            bf16x8 q0 = qread(0);
-            bf16x8 k1 = *(const MLA_LDS bf16x8*)(lr + kr[1]);
-            bf16x8 q1 = qread(1);
-            mfma32_v_first(st, k0, q0);
-            k0 = *(const MLA_LDS bf16x8*)(lr + kr[2]);
-            q0 = qread(2);
-            mfma32_v(st, k1, q1);
-            k1 = *(const MLA_LDS bf16x8*)(lr + kr[3]);
-            q1 = qread(3);
-            mfma32_v(st, k0, q0);
-            mfma32_v(st, k1, q1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        auto cread = [&](int s2) -> i32x4 {
-            return *(const MLA_LDS i32x4*)(lc + kb[s2 & 7] + 256 * (s2 >> 3));
+        const MLA_LDS uint8_t* lr = lds_rope + sc * kRopeSB;
+        auto cread = [&](int p2) -> i32x4 {
+            return *(const MLA_LDS i32x4*)(lc + (kb0 ^ ((p2 & 7) << 5)) + 256 * (p2 >> 3));
         };
-        i32x4 cw[2];
-        cw[0] = cread(0);
-        f32x16 ag;
-        static_for<0, 4>([&](auto gc) {
-            constexpr int g = decltype(gc)::value;
-            float scg[16];
-            load_scales(sc, g, scg);
-            static_for<0, 4>([&](auto uc) {
-                constexpr int u = decltype(uc)::value;
-                constexpr int s2 = 4 * g + u;  // code pair: steps 2 s2, 2 s2 + 1
-                if (s2 + 1 < 16) cw[(s2 + 1) & 1] = cread(s2 + 1);
-                const i32x4 w = cw[s2 & 1];
-                const bf16x8 a0 = fp8x8_to_bf16(w[0], w[1]);
-                const bf16x8 a1 = fp8x8_to_bf16(w[2], w[3]);
-                if (u == 0) mfma32_v_first<true>(ag, a0, qf[2 * s2]);
-                else mfma32_v<true>(ag, a0, qf[2 * s2]);
-                mfma32_v<true>(ag, a1, qf[2 * s2 + 1]);
-                __builtin_amdgcn_sched_barrier(0);
-            });
-            mfma_result_wait(ag);  // before the VALU reads the group product
+        auto sread = [&](int g, int c) -> f32x4 {  // scales of group g, tokens of st[4c .. 4c + 3]
+            return *(const MLA_LDS f32x4*)((const MLA_LDS uint8_t*)&sm.sct[sc][g][0] + 16 * half + 32 * c);
+        };
+        bf16x8 kro[4], qro[4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) st[i] = fmaf(scg[i], ag[i], st[i]);
+        for (int u = 0; u < 4; ++u) {
+            kro[u] = *(const MLA_LDS bf16x8*)(lr + (kr0 ^ (u << 5)));
+            qro[u] = qread(u);
+        }
+        i32x4 cw[3];
+        cw[0] = cread(0);
+        cw[1] = cread(1);
+        bf16x8 ka[2];   // widened operand of latent step L in ka[L & 1]
+        f32x16 st, ag[2];
+        f32x4 scr[4];   // scales of one group, chunk c for st[4c .. 4c + 3]
+        auto widen = [&](int L) -> bf16x8 {
+            const i32x4& w = cw[(L >> 1) % 3];
+            return (L & 1) ? fp8x8_to_bf16(w[2], w[3]) : fp8x8_to_bf16(w[0], w[1]);
+        };
+        static_for<0, 4 + 32>([&](auto sc_) {
+            constexpr int s = decltype(sc_)::value;
+            if constexpr (s < 4) {
+                if (s == 0) mfma32_v_first(st, kro[0], qro[0]);
+                else mfma32_v(st, kro[s], qro[s]);
+                if constexpr (s == 3) ka[0] = widen(0);
+            } else {
+                constexpr int L = s - 4, g = L >> 3, e = L & 7;
+                // ka was just written by VALU converts: FRESH leads with the
+                // two wait states an MFMA operand read needs after them
+                if (e == 0) mfma32_v_first<true>(ag[g & 1], ka[L & 1], qf[L]);
+                else mfma32_v<true>(ag[g & 1], ka[L & 1], qf[L]);
+                // code pair L / 2 + 2, read two pairs ahead of its first use
+                if constexpr ((L & 1) == 0 && (L >> 1) + 2 < 16) cw[((L >> 1) + 2) % 3] = cread((L >> 1) + 2);
+                if constexpr (L + 1 < 32) ka[(L + 1) & 1] = widen(L + 1);
+                // scale FMAs of the previous group, chunk c at e = c + 3; then
+                // chunk c of this group's scales replaces the consumed one
+                if constexpr (g >= 1 && e >= 3 && e < 7) {
+                    constexpr int c = e - 3;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        st[4 * c + k] = fmaf(scr[c][k], ag[(g - 1) & 1][4 * c + k], st[4 * c + k]);
+                }
+                if constexpr (e >= 4) scr[e - 4] = sread(g, e - 4);
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
+        {
+            // the last group's scale FMAs, after its product has landed;
+            // then the first output group's scales, read under the softmax
+            mfma_result_wait(ag[1]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) st[4 * c + k] = fmaf(scr[c][k], ag[1][4 * c + k], st[4 * c + k]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) scr[c] = sread(0, c);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 
         // ---- online softmax (log2 domain, lagging reference max) ----------
         if (cnt < kSub) {
@@ -491,10 +509,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
                 if (tok >= cnt) st[i] = -INFINITY;
             }
         }
-        float mx = fmaxf(fmaxf(st[0], st[1]), st[2]);
+        float mt3[5];
 #pragma unroll
-        for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, st[i]), st[i + 1]);
-        mx = fmaxf(mx, st[15]);
+        for (int k = 0; k < 5; ++k) mt3[k] = fmaxf(fmaxf(st[3 * k], st[3 * k + 1]), st[3 * k + 2]);
+        float mx = fmaxf(fmaxf(fmaxf(mt3[0], mt3[1]), mt3[2]), fmaxf(fmaxf(mt3[3], mt3[4]), st[15]));
         mx = xhalf_max(mx) * sl2;
         // a head whose max grew by more than kLag moves its reference;
         // accumulators of heads that had one rescale
@@ -507,49 +525,55 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         }
         if (grow) m = mx;
         const float nm = (m == -INFINITY) ? 0.f : -m;
-        float ps = 0.f;
+        float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(st[i], sl2, nm));
-            st[i] = e;
-            ps += e;
+        for (int i = 0; i < 16; i += 2) {
+            st[i] = __builtin_amdgcn_exp2f(fmaf(st[i], sl2, nm));
+            st[i + 1] = __builtin_amdgcn_exp2f(fmaf(st[i + 1], sl2, nm));
+            ps0 += st[i];
+            ps1 += st[i + 1];
         }
-        ps = xhalf_sum(ps);
-        l += ps;
+        l += xhalf_sum(ps0 + ps1);
 
         // ---- O^T += sum_g C_g^T . (P (.) scale_g)^T ----------------------------
-        // (the loads of sub-tile j+2 go out here, up to three per group)
-        static_for<0, 4>([&](auto gc) {
-            constexpr int g = decltype(gc)::value;
-            static_for<0, 3>([&](auto uc) {
-                constexpr int kk = 3 * g + decltype(uc)::value;
-                if constexpr (kk < kLoads) {
-                    if (SPARSE) {
-                        if (do_load) load_one(ld, SL{}, std::integral_constant<int, kk>{});
-                    } else {
-                        load_one(ld, SL{}, std::integral_constant<int, kk>{});
-                    }
+        // A flat schedule of 32 MFMAs u (group g = u / 8, tile 4 g + q with
+        // q = u / 2 % 4, token half u % 2).  Around each MFMA: the widening
+        // of the next one's V^T codes, the transposing read three ahead, the
+        // scaled probabilities of the next group, and (one in three) a load of
+        // sub-tile j+2.
+        auto vread8 = [&](int u) -> i32x2 {
+            const int g = u >> 3, q = (u >> 1) & 3, jj = u & 1;
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (MLA_LDS i32x2*)(lc + (vb0 ^ ((8 * (g & 1) + 2 * q) << 4)) + 256 * (g >> 1) + 8192 * jj));
+        };
+        i32x2 vr[4];
+        bf16x8 va[2];     // widened V^T operand of MFMA u in va[u & 1]
+        bf16x8 pf[2][2];  // P (.) scale_g of group g in pf[g & 1][token half]
+        auto pscale = [&](int g, int c, const f32x4& sv) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) pf[g & 1][c >> 1][4 * (c & 1) + k] = (__bf16)(st[4 * c + k] * sv[k]);
+        };
+#pragma unroll
+        for (int u = 0; u < 3; ++u) vr[u] = vread8(u);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pscale(0, c, scr[c]);
+        va[0] = fp8x8_to_bf16(vr[0][0], vr[0][1]);
+        static_for<0, 32>([&](auto uc) {
+            constexpr int u = decltype(uc)::value, g = u >> 3, e = u & 7;
+            // va (and, for u = 0, pf) were written by VALU converts just before
+            mfma32_acc<true>(acc[4 * g + ((u >> 1) & 3)], va[u & 1], pf[g & 1][u & 1]);
+            if constexpr (u + 3 < 32) vr[(u + 3) & 3] = vread8(u + 3);
+            if constexpr (u + 1 < 32) va[(u + 1) & 1] = fp8x8_to_bf16(vr[(u + 1) & 3][0], vr[(u + 1) & 3][1]);
+            // the next group's scaled probabilities: chunk c at e = c + 4,
+            // its scales read at e = c
+            if constexpr (g < 3 && e < 4) scr[e] = sread(g + 1, e);
+            if constexpr (g < 3 && e >= 4) pscale(g + 1, e - 4, scr[e - 4]);
+            if constexpr (u % 3 == 1 && u / 3 < kLoads) {
+                if (SPARSE) {
+                    if (do_load) load_one(ld, SL{}, std::integral_constant<int, u / 3>{});
+                } else {
+                    load_one(ld, SL{}, std::integral_constant<int, u / 3>{});
                 }
-            });
-            float scg[16];
-            load_scales(sc, g, scg);
-            bf16x8 pf[2];
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pf[jj][e] = (__bf16)(st[8 * jj + e] * scg[8 * jj + e]);
-            i32x2 vr[4][2];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-                    vr[q][jj] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (MLA_LDS i32x2*)(lc + vb[g & 1][q] + 256 * (g >> 1) + 8192 * jj));
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int mt = 4 * g + q;
-                mfma32_acc<true>(acc[mt], fp8x8_to_bf16(vr[q][0][0], vr[q][0][1]), pf[0]);
-                mfma32_acc<true>(acc[mt], fp8x8_to_bf16(vr[q][1][0], vr[q][1][1]), pf[1]);
             }
             __builtin_amdgcn_sched_barrier(0);
         });
