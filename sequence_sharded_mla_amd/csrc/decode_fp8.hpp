@@ -502,7 +502,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- online softmax (log2 domain, lagging reference max) ----------
-        if (cnt < kSub) {
+        if (__builtin_expect(cnt < kSub, 0)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int tok = (i >> 2) * 8 + half * 4 + (i & 3);
@@ -517,7 +517,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         // a head whose max grew by more than kLag moves its reference;
         // accumulators of heads that had one rescale
         const bool grow = mx > m + kLag;
-        if (__any(grow && m != -INFINITY)) {
+        if (__builtin_expect(__any(grow && m != -INFINITY), 0)) {
             const float alpha = grow ? exp2f(m - mx) : 1.f;
 #pragma unroll
             for (int i = 0; i < kDvTiles; ++i) scale_acc(acc[i], alpha);

@@ -387,7 +387,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
             constexpr int s = decltype(sc_)::value;
             if constexpr (s == 0) {
                 // only a partial or masked sub-tile needs masking
-                if (cnt < kSub) {
+                if (__builtin_expect(cnt < kSub, 0)) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int tok = (i >> 2) * 8 + half * 4 + (i & 3);
@@ -407,7 +407,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
                 // the order).  A head whose max grew by more than kLag moves
                 // its reference; accumulators of heads that had one rescale.
                 const bool grow = mx > m + kLag;
-                if (__any(grow && m != -INFINITY)) {
+                if (__builtin_expect(__any(grow && m != -INFINITY), 0)) {
                     const float alpha = grow ? exp2f(m - mx) : 1.f;
 #pragma unroll
                     for (int i = 0; i < kDvTiles; ++i) scale_acc(acc[i], alpha);
