@@ -16,6 +16,11 @@ program order:
 Wait states are counted as one per instruction, N + 1 per `s_nop N`.  The
 walk is linear (it does not follow branches): a regression guard for the
 straight-line loop bodies, not a proof.
+
+The direct global->LDS loads are inline asm that write M0 (the LDS base).
+The compiler is told M0 is clobbered, but M0 is a register it may also
+allocate; in a kernel whose asm writes M0, no instruction the compiler
+emits may read or write M0, or a value it keeps there would be overwritten.
 """
 
 import os
@@ -61,6 +66,41 @@ def _instructions(asm):
         parts = line.split(None, 1)
         cur.append((parts[0], parts[1] if len(parts) > 1 else ""))
     return kernels
+
+
+_M0 = re.compile(r"\bm0\b")
+
+
+def _m0_uses(asm):
+    """Per kernel: (number of inline-asm lines naming m0, compiler-emitted
+    instructions naming m0)."""
+    out, cur, inasm = {}, None, False
+    for raw in asm.split("\n"):
+        s = raw.strip()
+        if s.startswith(";;#ASMSTART"):
+            inasm = True
+            continue
+        if s.startswith(";;#ASMEND"):
+            inasm = False
+            continue
+        line = s.split(";")[0].strip()
+        if not line:
+            continue
+        if line.endswith(":") and line.startswith("_Z"):
+            cur = out.setdefault(line[:-1], [0, []])
+            continue
+        if cur is None or line.startswith(".") or not _M0.search(line):
+            continue
+        if inasm:
+            cur[0] += 1
+        else:
+            cur[1].append(line)
+    return out
+
+
+def _m0_conflicts(uses):
+    return [f"{k}: compiler-emitted '{ins[0]}' in a kernel whose asm writes m0"
+            for k, (n_asm, ins) in uses.items() if n_asm and ins]
 
 
 def _wait_states(mn, ops):
@@ -158,3 +198,27 @@ def test_checker_catches_a_missing_wait_state():
             ("s_nop", "7"), ("s_nop", "7"),
             ("v_add_f32", "v40, v18, v41")]
     assert _check("k", good) == []
+
+
+def test_m0_left_to_the_asm(device_asm):
+    uses = _m0_uses(device_asm)
+    writers = [k for k, (n, _) in uses.items() if n and ("decode_mfma" in k)]
+    assert len(writers) >= 3, "the decode kernels' direct-to-LDS loads were expected to set m0 in asm"
+    problems = _m0_conflicts(uses)
+    assert not problems, "\n".join(problems[:20])
+
+
+def test_m0_checker_flags_a_compiler_use():
+    asm = "\n".join([
+        "_Zk:",
+        ";;#ASMSTART",
+        "s_mov_b32 m0, s4",
+        "global_load_lds_dwordx4 v1, s[2:3]",
+        ";;#ASMEND",
+        "v_writelane_b32 v5, s6, m0",
+        "_Zq:",
+        "s_mov_b32 m0, s7",
+    ])
+    uses = _m0_uses(asm)
+    assert uses["_Zk"][0] == 1 and len(uses["_Zk"][1]) == 1
+    assert len(_m0_conflicts(uses)) == 1   # _Zq uses m0 only in compiler code: no asm writer
