@@ -97,11 +97,19 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
         if ((st = launch_status()) != MLA_OK) return st;
     }
     const uint32_t n_items = uint32_t(plan.items_max);
-    const bool mfma_bf16 = d->kv_dtype == MLA_BF16 && d->topk == 0 && d->num_heads == 128;
+    // bf16 dense: every supported head count (16 pads to 32); 128 / H' output
+    // dimension parts per head group keep all four waves busy
+    const bool mfma_bf16 = d->kv_dtype == MLA_BF16 && d->topk == 0 &&
+                           (d->num_heads == 16 || d->num_heads == 32 || d->num_heads == 64 || d->num_heads == 128);
     const bool mfma_fp8 = d->kv_dtype == MLA_FP8_DS && (d->num_heads == 64 || d->num_heads == 128) &&
                           d->topk <= mfma::kMaxTopk;
     if (mfma_bf16) {
-        hipLaunchKernelGGL(mfma::decode_mfma_bf16_kernel, dim3(n_items), dim3(256), 0, s, p);
+        if (d->num_heads == 128)
+            hipLaunchKernelGGL(mfma::decode_mfma_bf16_kernel<1>, dim3(n_items), dim3(256), 0, s, p);
+        else if (d->num_heads == 64)
+            hipLaunchKernelGGL(mfma::decode_mfma_bf16_kernel<2>, dim3(n_items), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL(mfma::decode_mfma_bf16_kernel<4>, dim3(n_items), dim3(256), 0, s, p);
     } else if (mfma_fp8) {
         const bool sparse = d->topk > 0;
         if (d->num_heads == 64) {

@@ -1,16 +1,22 @@
 // Matrix-core partial decode for a bf16 latent cache (gfx950).
 //
 // One workgroup of four waves handles one (shard, request, query token,
-// chunk) row and all 128 query heads; wave w owns heads [32w, 32w + 32).  The
-// shard's local tokens stream through a ring of four 32-token sub-tiles in
-// LDS, filled by direct global->LDS loads (global_load_lds_dwordx4) three
-// sub-tiles ahead.  Per sub-tile and wave:
+// chunk) row and all its query heads.  The shard's local tokens stream
+// through a ring of four 32-token sub-tiles in LDS, filled by direct
+// global->LDS loads (global_load_lds_dwordx4) three sub-tiles ahead.  The
+// four waves split the heads into groups of 32 and, when there are fewer
+// than four groups, the 512 output dimensions into DS = 128 / H' parts
+// (H' = H padded to a multiple of 32): wave w owns head group w % (4 / DS)
+// and output tiles [16 d / DS, 16 (d + 1) / DS) with d = w / (4 / DS).  The
+// waves of one head group all form its scores (the work the split repeats);
+// the loads, the ring and its layout are the same for every head count.
+// Per sub-tile and wave:
 //
 //   S^T[32 tok x 32 heads] = K[32 x 576] . Q^T[576 x 32]        36 MFMA 32x32x16
 //   online softmax per head: the scores of one head sit in one lane (and its
 //   partner lane l^32), so the running max / sum need one cross-lane step
-//   O^T[512 x 32 heads]  += V^T[512 x 32 tok] . P^T[32 tok x 32 heads]
-//                                                               32 MFMA 32x32x16
+//   O^T[512/DS x 32 heads] += V^T[512/DS x 32 tok] . P^T[32 tok x 32 heads]
+//                                                         32/DS MFMA 32x32x16
 //
 // The loop is software pipelined: iteration j issues the score product of
 // sub-tile j+1 together with the softmax of sub-tile j, then the output
@@ -70,15 +76,21 @@ struct alignas(16) SmemBf16 {
     uint8_t qrope[kQRopeB];  // [head][8 chunks of 16 B], chunk c at c ^ ((head >> 1) & 7)
 };
 
+template <int DS>
 __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p) {
+    static_assert(DS == 1 || DS == 2 || DS == 4, "output dimension splits");
+    constexpr int kHG = 4 / DS;             // head groups of 32
+    constexpr int kDvT = kDvTiles / DS;     // 32-dim output tiles per wave
     __shared__ SmemBf16 sm;
     RowId id;
     if (!work_item(p, blockIdx.x, id)) return;  // past the last planned item
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int half = lane >> 5;
-    const int col = lane & 31;  // head within the wave (S^T, O^T columns)
-    const int head = wave * 32 + col;
+    const int col = lane & 31;  // head within the group (S^T, O^T columns)
+    const int dsp = DS == 1 ? 0 : wave / kHG;  // output dimension part of this wave
+    const int head = DS == 1 ? wave * 32 + col : (wave % kHG) * 32 + col;
+    const bool head_ok = DS < 4 || head < p.H;  // 16 heads: the group's upper half is padding
     const int s = p.shard_begin + id.s_rel;
     const int32_t* bt = p.block_tables + (size_t(id.s_rel) * p.B + id.b) * p.max_blocks;
 
@@ -100,21 +112,24 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     const int n_pad = (n_sub + kRing - 1) / kRing * kRing;
 
     // ---- Q^T fragments: head `head`, dims 16 ks + 8 half .. + 8 ------------
-    // latent part in registers, rope part in LDS (each wave writes and later
-    // reads only its own heads, so program order within the wave suffices)
+    // latent part in registers, rope part in LDS, written by the group's
+    // first wave (the barrier before the first score product orders it
+    // before the other waves' reads); padding heads are zero
     bf16x8 qf[kQLatSteps];
     const int qr_off = head * kRopeB;
     const int qr_sw = (head >> 1) & 7;
     {
         const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
-            static_cast<const uint16_t*>(p.q) + (size_t(id.qi) * p.H + head) * kDk);
+            static_cast<const uint16_t*>(p.q) + (size_t(id.qi) * p.H + (head_ok ? head : 0)) * kDk);
 #pragma unroll
-        for (int ks = 0; ks < kQLatSteps; ++ks) qf[ks] = qrow[2 * ks + half];
+        for (int ks = 0; ks < kQLatSteps; ++ks) qf[ks] = head_ok ? qrow[2 * ks + half] : bf16x8{};
+        if (DS == 1 || dsp == 0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = 2 * u + half;
-            *(MLA_LDS bf16x8*)((MLA_LDS uint8_t*)sm.qrope + qr_off + ((c ^ qr_sw) << 4)) =
-                qrow[2 * (kQLatSteps + u) + half];
+            for (int u = 0; u < 4; ++u) {
+                const int c = 2 * u + half;
+                *(MLA_LDS bf16x8*)((MLA_LDS uint8_t*)sm.qrope + qr_off + ((c ^ qr_sw) << 4)) =
+                    head_ok ? qrow[2 * (kQLatSteps + u) + half] : bf16x8{};
+            }
         }
     }
 
@@ -217,9 +232,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     }
     int32_t blk_ahead = block_of(kAhead);  // block id of the next sub-tile to load
 
-    f32x16 acc[kDvTiles];
+    f32x16 acc[kDvT];
 #pragma unroll
-    for (int i = 0; i < kDvTiles; ++i) acc[i] = f32x16{};
+    for (int i = 0; i < kDvT; ++i) acc[i] = f32x16{};
     float m = -INFINITY;  // reference max of this head, log2 domain
     float l = 0.f;        // sum of 2^(s - m)
     const float sl2 = p.scale * 1.4426950408889634f;
@@ -238,11 +253,15 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         const int g16 = lane >> 4, s16 = lane & 15;
         const int c0 = 2 * (g16 & 1) + ((s16 & 3) >> 1);  // chunk within a 32-dim tile
         const int bsub = (s16 & 1) * 8;                  // byte within the chunk
+        // this wave's first output tile: whole 256-byte dimension groups
+        // (kDvT is a multiple of 4), a plain offset outside the swizzle
+        const int dgrp = 256 * dsp * (kDvT / 4);
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
             const int t = 4 * (g16 >> 1) + (s16 >> 2) + 8 * w;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) vb[w][q] = lat_row(0, t) + bsub + (((4 * q + c0) ^ swz(t)) << 4);
+            for (int q = 0; q < 4; ++q)
+                vb[w][q] = lat_row(0, t) + dgrp + bsub + (((4 * q + c0) ^ swz(t)) << 4);
         }
     }
     const MLA_LDS uint8_t* lds = (const MLA_LDS uint8_t*)sm.ring;
@@ -274,10 +293,13 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     // LDS and are dead early), then the 32 latent steps
     auto step_ks = [](int r) { return r < 4 ? kQLatSteps + r : r - 4; };
 
-    // ---- main loop: one flat schedule of 68 MFMA slots per sub-tile ----------
+    // ---- main loop: one flat schedule of 36 + 32/DS MFMA slots per sub-tile --
     // Iteration j issues the score product of sub-tile j+1 (36 MFMAs) and the
-    // output product of sub-tile j (32 MFMAs: 16 output tiles x 2 token
-    // halves), with the softmax of sub-tile j spread over the slots.  A wave issues in order,
+    // output product of sub-tile j (32/DS MFMAs: the wave's output tiles x 2
+    // token halves), with the softmax of sub-tile j spread over the slots.
+    // The layout below is the one for all 16 tiles (68 slots); with fewer
+    // tiles the token-half-1 phase is shorter and the second half's
+    // probabilities are formed two slots apart.  A wave issues in order,
     // and about four independent VALU instructions (or two exponentials)
     // execute under one 32-cycle MFMA; beyond that each costs the matrix core
     // idle cycles, so the VALU work is dealt out at that rate:
@@ -296,18 +318,34 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     // dropped.
     constexpr int kAK = 2;  // K fragments read this many score steps ahead
     constexpr int kAV = 2;  // V^T fragments read this many output MFMAs ahead
-    constexpr int kSlots = kQSteps + 2 * kDvTiles;  // 68
-    // slot of score step r, and of output MFMA u = 16 jj + mt
-    constexpr auto qk_slot = [](int r) { return r < 14 ? r : r < 30 ? 15 + 2 * (r - 14) : 48 + 3 * (r - 30); };
+    constexpr int kSlots = kQSteps + 2 * kDvT;  // 68, 52 or 44
+    constexpr int kC0 = 14 + 2 * kDvT;          // first slot of the token-half-1 phase
+    // slot of score step r, and of output MFMA u = kDvT jj + mt.  Slots
+    // 0..13 hold score steps 0..13; then token half 0's output MFMAs
+    // alternate with score steps 14 ..; then token half 1's output MFMAs
+    // are spread among the remaining score steps.
+    constexpr auto qk_slot = [](int r) {
+        if (r < 14) return r;
+        if (r < 14 + kDvT) return 15 + 2 * (r - 14);
+        const int k = r - 14 - kDvT;  // score steps left for the last phase
+        if constexpr (DS == 1) return kC0 + 2 + 3 * k;                 // S after each PV pair
+        else if constexpr (DS == 2) return kC0 + 3 * (k >> 1) + 2 * (k & 1);  // S P S
+        else return k < 16 ? kC0 + 5 * (k >> 2) + ((k & 3) < 2 ? (k & 3) : (k & 3) + 1)  // S S P S S
+                           : kC0 + 20 + (k - 16);
+    };
     constexpr auto pv_slot = [](int u) {
-        const int mt = u & 15;
-        return u < 16 ? 14 + 2 * mt : mt < 12 ? 46 + 3 * (mt >> 1) + (mt & 1) : 52 + mt;
+        const int mt = u % kDvT;
+        if (u < kDvT) return 14 + 2 * mt;
+        if constexpr (DS == 1) return mt < 12 ? kC0 + 3 * (mt >> 1) + (mt & 1) : kC0 + 6 + mt;
+        else if constexpr (DS == 2) return mt < 7 ? kC0 + 3 * mt + 1 : kC0 + 21;
+        else return kC0 + 5 * mt + 2;
     };
     // the probability pair p (elements 2p, 2p + 1): fma, exp2, sum + pack slots
-    constexpr auto fma_slot = [](int p) { return p < 4 ? 4 + 2 * p : 16 + 4 * (p - 4); };
-    constexpr auto exp_slot = [](int p) { return p < 4 ? 5 + 2 * p : 18 + 4 * (p - 4); };
-    constexpr auto sum_slot = [](int p) { return p < 4 ? 6 + 2 * p : 20 + 4 * (p - 4); };
-    constexpr int kSumSlot = 34;                        // normaliser
+    constexpr auto fma_slot = [](int p) { return p < 4 ? 4 + 2 * p : DS == 1 ? 16 + 4 * (p - 4) : 12 + 2 * (p - 4); };
+    constexpr auto exp_slot = [](int p) { return p < 4 ? 5 + 2 * p : DS == 1 ? 18 + 4 * (p - 4) : 13 + 2 * (p - 4); };
+    constexpr auto sum_slot = [](int p) { return p < 4 ? 6 + 2 * p : DS == 1 ? 20 + 4 * (p - 4) : 14 + 2 * (p - 4); };
+    constexpr int kSumSlot = DS == 1 ? 34 : 21;         // normaliser
+    static_assert(sum_slot(7) < pv_slot(kDvT), "token half 1 probabilities before their first MFMA");
     constexpr auto load_slot = [](int k) { return 15 + 3 * k; };  // the nine loads of sub-tile j+3
 
     f32x16 sA, sB;
@@ -371,10 +409,10 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         bf16x8 vf[kAV + 1];
         bf16x8 pf[2];
         auto pv_step = [&](int u, bool fresh) {
-            if (u + kAV < 2 * kDvTiles) vf[(u + kAV) % (kAV + 1)] = vread(sc, (u + kAV) >> 4, (u + kAV) & 15);
-            const int mt = u & 15;
-            if (fresh) mfma32_acc<true>(acc[mt], vf[u % (kAV + 1)], pf[u >> 4]);
-            else mfma32_acc(acc[mt], vf[u % (kAV + 1)], pf[u >> 4]);
+            if (u + kAV < 2 * kDvT) vf[(u + kAV) % (kAV + 1)] = vread(sc, (u + kAV) / kDvT, (u + kAV) % kDvT);
+            const int mt = u % kDvT;
+            if (fresh) mfma32_acc<true>(acc[mt], vf[u % (kAV + 1)], pf[u / kDvT]);
+            else mfma32_acc(acc[mt], vf[u % (kAV + 1)], pf[u / kDvT]);
         };
 
         // softmax of sub-tile j (log2 domain; the reference max m may lag the
@@ -410,7 +448,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
                 if (__builtin_expect(__any(grow && m != -INFINITY), 0)) {
                     const float alpha = grow ? exp2f(m - mx) : 1.f;
 #pragma unroll
-                    for (int i = 0; i < kDvTiles; ++i) scale_acc(acc[i], alpha);
+                    for (int i = 0; i < kDvT; ++i) scale_acc(acc[i], alpha);
                     l *= alpha;
                 }
                 if (grow) m = mx;
@@ -444,11 +482,11 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
             static_for<0, kQSteps>([&](auto rc) {
                 if constexpr (qk_slot(decltype(rc)::value) == s) qk_step(decltype(rc)::value);
             });
-            static_for<0, 2 * kDvTiles>([&](auto uc) {
+            static_for<0, 2 * kDvT>([&](auto uc) {
                 constexpr int u = decltype(uc)::value;
                 // the first output MFMA reads probabilities packed by VALU
                 // converts just before: it leads with the two wait states
-                if constexpr (pv_slot(u) == s) pv_step(u, u == 0 || u == kDvTiles);
+                if constexpr (pv_slot(u) == s) pv_step(u, u == 0 || u == kDvT);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -477,19 +515,20 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     const float lse = empty ? -INFINITY : (m + log2f(l)) * 0.6931471805599453f;
     // whole row: the shard's output; a chunk of a split row: its partial slot
     const bool direct = id.slot < 0;
-    const size_t orow = direct ? size_t(id.row) * p.H + head : size_t(id.slot) * p.H + head;
+    const size_t orow0 = (direct ? size_t(id.row) : size_t(id.slot)) * p.H + (head - col);  // group's head 0
+    const int dim0 = dsp * (kLatent / DS);  // this wave's first output dimension
     // chunk partials stay float32 whatever the output dtype
     if (direct && p.out_dtype == MLA_BF16) {
         // staged through the ring's LDS once every wave is past its last read
         static_assert(sizeof(sm) >= 4 * 32 * 1024, "staging fits the LDS of the ring");
         __syncthreads();
-        store_rows_bf16<1>(acc, inv, (MLA_LDS uint8_t*)&sm + wave * 32 * 1024,
-                            static_cast<uint16_t*>(p.o_out) + (orow - col) * kLatent,
-                            lane);
-    } else {
-        float* o = static_cast<float*>(direct ? p.o_out : p.ws_o) + orow * kLatent;
+        store_tiles_bf16<kDvT>(acc, inv, (MLA_LDS uint8_t*)&sm + wave * 32 * 1024,
+                               static_cast<uint16_t*>(p.o_out) + orow0 * kLatent + dim0,
+                               min(32, p.H - (head - col)), lane);
+    } else if (head_ok) {
+        float* o = static_cast<float*>(direct ? p.o_out : p.ws_o) + (orow0 + col) * kLatent + dim0;
 #pragma unroll
-        for (int mt = 0; mt < kDvTiles; ++mt)
+        for (int mt = 0; mt < kDvT; ++mt)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int d = 32 * mt + 8 * q4 + 4 * half;
@@ -498,7 +537,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
                                 acc[mt][4 * q4 + 2] * inv, acc[mt][4 * q4 + 3] * inv);
             }
     }
-    if (half == 0) (direct ? p.lse_out : p.ws_lse)[orow] = lse;
+    if (half == 0 && dsp == 0 && head_ok) (direct ? p.lse_out : p.ws_lse)[orow0 + col] = lse;
 }
 
 }  // namespace mfma

@@ -251,6 +251,39 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16 (&acc)[kDvTiles], f
     }
 }
 
+// O^T tiles of one wave (32 heads x NT 32-dim tiles, scaled by inv) to bf16
+// rows out + r * kLatent for heads r < rows: each lane packs its values
+// into a per-head row of the staging area (16-byte chunks XOR-swizzled by
+// the head), then every lane stores 16 contiguous bytes of a row.
+template <int NT>
+__device__ __forceinline__ void store_tiles_bf16(const f32x16 (&acc)[NT], float inv,
+                                                 MLA_LDS uint8_t* stage, uint16_t* out, int rows,
+                                                 int lane) {
+    static_assert(NT == 4 || NT == 8 || NT == 16, "output tiles per wave");
+    constexpr int kRB = NT * 64;            // bytes of a staged row
+    constexpr int kCh = kRB / 16;           // 16-byte chunks per staged row
+    constexpr int kRowsPerOp = 64 / kCh;    // staged rows per 64-lane read
+    const int col = lane & 31, half = lane >> 5;
+    MLA_LDS uint8_t* wrow = stage + col * kRB + 8 * half;
+    const int rsub = lane / kCh, j = lane % kCh;
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x16& a = acc[mt];
+            i32x2 w;
+            w[0] = int(bf16x2_rne(a[4 * q4 + 0] * inv, a[4 * q4 + 1] * inv));
+            w[1] = int(bf16x2_rne(a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv));
+            *(MLA_LDS i32x2*)(wrow + (((4 * mt + q4) ^ (col & (kCh - 1))) << 4)) = w;
+        }
+#pragma unroll
+    for (int k = 0; k < 32 / kRowsPerOp; ++k) {
+        const int r = k * kRowsPerOp + rsub;
+        const i32x4 v = *(const MLA_LDS i32x4*)(stage + r * kRB + ((j ^ (r & (kCh - 1))) << 4));
+        if (r < rows) *reinterpret_cast<i32x4*>(out + size_t(r) * kLatent + 8 * j) = v;
+    }
+}
+
 // Growth of a head's running max (log2 units) tolerated before the
 // accumulators are rescaled: probabilities are formed against a reference
 // max that may lag the true running max by at most this much, so they stay

@@ -36,7 +36,8 @@ def test_tiny_f32_full():
     assert errs["lse"] < 2e-6 and errs["lse_shards"] < 2e-6
 
 
-@pytest.mark.parametrize("kv,heads", [("bf16", 128), ("fp8_ds", 64), ("fp8_ds", 128), ("f32", 16)])
+@pytest.mark.parametrize("kv,heads", [("bf16", 128), ("bf16", 64), ("bf16", 16), ("fp8_ds", 64), ("fp8_ds", 128),
+                                      ("f32", 16)])
 def test_tile_boundary_lengths(kv, heads):
     """Local lengths at and around the 32-token sub-tile and the 64-token
     block: requests whose context puts 31, 32, 33, 63, 64, 65, 127, 128 and

@@ -14,6 +14,7 @@ draws stand in for them):
                        4 shards, float32 query and cache
   dense_bf16_32k       32 requests, 128 heads, context 32768, 8 shards,
                        bf16 query and cache
+  dense_bf16_h64_32k   the same with 64 heads (the gathered-head pad)
   dense_fp8_mixed      64 requests, 64 heads, context uniform on
                        [4096, 131072], 8 shards, fp8 cache
   long_fp8_1m          4 requests, 64 heads, context 1048576, 8 shards,
@@ -77,6 +78,9 @@ SPECS = {
     "dense_bf16_32k": Spec("dense_bf16_32k", batch=32, q_len=1, heads=128,
                            n_shards=8, q_dtype="bf16", kv_dtype="bf16",
                            out_dtype="bf16", context=32768, seed=202),
+    "dense_bf16_h64_32k": Spec("dense_bf16_h64_32k", batch=32, q_len=1, heads=64,
+                               n_shards=8, q_dtype="bf16", kv_dtype="bf16",
+                               out_dtype="bf16", context=32768, seed=212),
     "dense_fp8_mixed": Spec("dense_fp8_mixed", batch=64, q_len=1, heads=64,
                             n_shards=8, q_dtype="bf16", kv_dtype="fp8_ds",
                             out_dtype="bf16", ctx_range=(4096, 131072),
