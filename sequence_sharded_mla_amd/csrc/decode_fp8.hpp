@@ -278,32 +278,37 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         int last;
         int v;  // real rows (<= 0: padding)
     };
-    // block id of dense sub-tile j (-1 past the range, whose entry is not
-    // read).  The main loop reads it one iteration ahead, at a point where no
-    // LDS read is in flight, so that waiting for it waits for nothing else.
+    // block id of dense sub-tile j.  The main loop reads it one iteration
+    // ahead, at a point where no LDS read is in flight, so that waiting for it
+    // waits for nothing else.  A padding sub-tile reads the entry of the
+    // chunk's last row (in the table; its value is unused).
+    const uint32_t last_tok = uint32_t(max(tok1 - 1, 0));
     auto block_of = [&](int j) -> int32_t {
-        const int32_t j0 = tok0 + j * kSub;
-        return (!SPARSE && j0 < tok1) ? btc[uint32_t(j0) / kBlock] : -1;
+        if constexpr (SPARSE) return -1;
+        const uint32_t j0 = uint32_t(tok0 + j * kSub);
+        return btc[min(j0, last_tok) / kBlock];
     };
+    // Dense: branch free, the source a select between the block's row and the
+    // zero row and the validity test one unsigned compare (a negative id wraps
+    // past every pool size an int32 id can name).
+    const uint32_t pool32 =
+        p.pool_blocks > int64_t(0x80000000) ? 0x80000000u : uint32_t(p.pool_blocks);
     auto prep = [&](int j, int32_t blk, auto slot_c) -> SrcF {
         constexpr int slot = decltype(slot_c)::value;
         const int32_t j0 = tok0 + j * kSub;
         const int v = min(kSub, tok1 - j0);  // <= 0: padding
-        SrcF r{kZeroRow, j0, (v > 0 ? v : 1) - 1, v};
-        if (!SPARSE) {
-            bool bad = false;
-            r.last = 0;
-            if (v > 0) {
-                if (blk >= 0 && blk < p.pool_blocks) {
-                    r.src = p.kv + (int64_t(blk) * kBlock + (uint32_t(j0) % kBlock)) * kRowF;
-                    r.last = v - 1;
-                } else {
-                    bad = true;
-                }
-            }
+        if constexpr (SPARSE) {
+            return SrcF{kZeroRow, j0, (v > 0 ? v : 1) - 1, v};
+        } else {
+            const bool bad = v > 0 && uint32_t(blk) >= pool32;
+            const bool use = v > 0 && !bad;
+            const uint64_t mask = 0ull - uint64_t(use);  // all ones when the row is read
+            const uint64_t row = reinterpret_cast<uint64_t>(p.kv) +
+                                 (uint64_t(uint32_t(blk) & uint32_t(mask)) * kBlock + (uint32_t(j0) % kBlock)) * kRowF;
+            const uint64_t src = (row & mask) | (reinterpret_cast<uint64_t>(kZeroRow) & ~mask);
             bad_slot[slot] = bad;
+            return SrcF{reinterpret_cast<const uint8_t*>(src), j0, max(v - 1, 0) & int(uint32_t(mask)), v};
         }
-        return r;
     };
     // Load kk of this wave for the sub-tile of r in `slot`: kk < kCodeLoads a
     // code load, then kRopeLoads rope loads, then the scale load.
@@ -414,7 +419,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         // issue path has no branch.
         using SL = std::integral_constant<int, (sc + 2) % kRingF>;
         const bool do_load = !SPARSE || j + 2 < n_pad;
-        const SrcF ld = j + 2 < n_pad ? prep(j + 2, blk_ahead, SL{}) : SrcF{kZeroRow, 0, 0, 0};
+        const SrcF ld = (!SPARSE || j + 2 < n_pad) ? prep(j + 2, blk_ahead, SL{}) : SrcF{kZeroRow, 0, 0, 0};
         const int cnt = bad_slot[sc] ? 0 : sub_count(j);
         bad_block |= bad_slot[sc];
         // group scales of sub-tile j, transposed to [group][token]

@@ -165,30 +165,34 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         const uint8_t* src;
         int last;
     };
-    // block id of sub-tile j (-1 for a padding sub-tile, whose table entry is
-    // not read).  The main loop reads it one iteration before its loads are
-    // issued: waiting for a scalar load right before them would stall every
-    // wave at the top of each iteration.
+    // block id of sub-tile j.  The main loop reads it one iteration before its
+    // loads are issued: waiting for a scalar load right before them would
+    // stall every wave at the top of each iteration.  A padding sub-tile reads
+    // the entry of the chunk's last row (in the table; its value is unused).
+    const uint32_t last_tok = uint32_t(max(tok1 - 1, 0));
     auto block_of = [&](int j) -> int32_t {
         const uint32_t j0 = uint32_t(tok0) + uint32_t(j) * kSub;
-        return j0 < uint32_t(tok1) ? btc[j0 / kBlock] : -1;
+        return btc[min(j0, last_tok) / kBlock];
     };
+    // Branch free: the source is a select between the block's row and the
+    // zero row, and the validity test one unsigned compare (a negative id
+    // wraps past every pool size an int32 id can name).  On the top-of-
+    // iteration path, a chain of branches and a 64-bit vector compare here
+    // held back the first K reads.
+    const uint32_t pool32 =
+        p.pool_blocks > int64_t(0x80000000) ? 0x80000000u : uint32_t(p.pool_blocks);
     auto source = [&](int j, int32_t blk, auto slot_c) -> Src {
         constexpr int slot = decltype(slot_c)::value;
         const uint32_t j0 = uint32_t(tok0) + uint32_t(j) * kSub;
-        const int v = min(kSub, tok1 - int(j0));  // <= 0: padding
-        Src r{kZeroRow, 0};
-        bool bad = false;
-        if (v > 0) {
-            if (blk >= 0 && blk < p.pool_blocks) {
-                r.src = p.kv + (int64_t(blk) * kBlock + (j0 % kBlock)) * kRowB;
-                r.last = v - 1;
-            } else {
-                bad = true;
-            }
-        }
+        const int v = tok1 - int(j0);  // rows left in the chunk (<= 0: padding)
+        const bool bad = v > 0 && uint32_t(blk) >= pool32;
+        const bool use = v > 0 && !bad;
+        const uint64_t mask = 0ull - uint64_t(use);  // all ones when the row is read
+        const uint64_t row = reinterpret_cast<uint64_t>(p.kv) +
+                             (uint64_t(uint32_t(blk) & uint32_t(mask)) * kBlock + (j0 % kBlock)) * kRowB;
+        const uint64_t src = (row & mask) | (reinterpret_cast<uint64_t>(kZeroRow) & ~mask);
         bad_slot[slot] = bad;
-        return r;
+        return Src{reinterpret_cast<const uint8_t*>(src), max(min(v, kSub) - 1, 0) & int(uint32_t(mask))};
     };
     // load k of this wave for a sub-tile in `slot`: k < 8 the latent part of
     // row 4k + w, k = 8 the rope parts of rows 8w .. 8w + 7.  Branch free:
@@ -380,7 +384,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         // row into that free slot (no sub-tile uses it again), so the issue
         // path has no branch.
         using SL = std::integral_constant<int, (sc + kAhead) % kRing>;
-        const Src ld = j + kAhead < n_pad ? source(j + kAhead, blk_ahead, SL{}) : Src{kZeroRow, 0};
+        const Src ld = source(j + kAhead, blk_ahead, SL{});
         // a bad block id's sub-tile holds zero rows: all its scores are
         // masked below; no early exit
         const int cnt = bad_slot[sc] ? 0 : sub_count(j);
