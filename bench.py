@@ -639,33 +639,54 @@ def main():
     torch.cuda.synchronize()
     assert mla_get_device_error(step.workspace) == 0
 
-    # Timed region: K steps, each after a 1 GiB fill (outside its events) that
+    # Timed region: K steps, each after a 1 GiB write (outside its events) that
     # evicts the 256 MB last-level cache, so no cache row of the previous step
-    # is served from it.  The step's time is its own events (partials, then
-    # merge); the fills run on the same stream between them.
+    # is served from it, then a 512 MiB read of a clean buffer (also outside
+    # the events) that pushes the write's dirty lines out of the cache: left
+    # there, their write-back to HBM would run during the step and compete
+    # with its reads.  The step's time is its own events (partials, then
+    # merge); the flush kernels run on the same stream between them.  The same
+    # K steps after the write alone are reported beside it.
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     evict = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    clean = torch.ones(1 << 27, dtype=torch.int32, device="cuda")  # 512 MiB
+
+    def timed_series(clean_read):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            evict.fill_(i & 0xff)
+            if clean_read:
+                clean.sum()
+            a, b, c = ev[i]
+            a.record(stream)
+            step.partials()
+            b.record(stream)
+            step.merge()
+            c.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        t_part = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        t_merge = np.array([e[1].elapsed_time(e[2]) for e in ev])
+        return t_part, t_merge, wall
+
     log(f"bench: timing {K} steps (cache flushed before each)")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        evict.fill_(i & 0xff)
-        a, b, c = ev[i]
-        a.record(stream)
-        step.partials()
-        b.record(stream)
-        step.merge()
-        c.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t_part = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    t_merge = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    t_part, t_merge, wall = timed_series(True)
     t_step = t_part + t_merge
     ms_per_step = float(np.mean(t_step))
-    del evict
     assert mla_get_device_error(step.workspace) == 0
+    flush_w = None
+    if not args.no_extras:
+        tw_part, tw_merge, _ = timed_series(False)
+        flush_w = {"note": "the same steps after the 1 GiB write alone (its dirty lines written back "
+                           "during the step)",
+                   "ms_per_step": round(float(np.mean(tw_part + tw_merge)), 4),
+                   "decode_partials_mean_ms": round(float(np.mean(tw_part)), 4),
+                   "decode_frac": round(launch_bytes / (float(np.mean(tw_part)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        assert mla_get_device_error(step.workspace) == 0
+    del evict, clean
 
     extras = not args.no_extras
     # Warm series (secondary): K steps back to back, no flush.
@@ -758,8 +779,10 @@ def main():
         "config": {"workload": sp.name, "batch": sp.batch, "q_len": sp.q_len, "heads": sp.heads,
                    "context": sp.context or list(sp.ctx_range), "n_shards": sp.n_shards,
                    "kv_cache": sp.kv_dtype, "topk": sp.topk, "block_size": 64},
-        "timing": "each step after a 1 GiB cache flush; ms_per_step = mean of the steps' HIP-event "
+        "timing": "each step after a 1 GiB write and a 512 MiB clean read (cache evicted, no dirty "
+                  "lines left), both outside the events; ms_per_step = mean of the steps' HIP-event "
                   "times (partials + merge)",
+        "write_flush_only": flush_w,
         "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 4),
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "kv_tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
