@@ -181,18 +181,32 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     // held back the first K reads.
     const uint32_t pool32 =
         p.pool_blocks > int64_t(0x80000000) ? 0x80000000u : uint32_t(p.pool_blocks);
-    auto source = [&](int j, int32_t blk, auto slot_c) -> Src {
+    // In three stages (validity, row address, select) so that the main loop
+    // can deal the scalar chain out over several MFMA slots.
+    struct SrcA {
+        uint32_t j0;
+        int v;
+        uint64_t mask;  // all ones when the row is read
+    };
+    auto source_a = [&](int j, int32_t blk, auto slot_c) -> SrcA {
         constexpr int slot = decltype(slot_c)::value;
         const uint32_t j0 = uint32_t(tok0) + uint32_t(j) * kSub;
         const int v = tok1 - int(j0);  // rows left in the chunk (<= 0: padding)
         const bool bad = v > 0 && uint32_t(blk) >= pool32;
-        const bool use = v > 0 && !bad;
-        const uint64_t mask = 0ull - uint64_t(use);  // all ones when the row is read
-        const uint64_t row = reinterpret_cast<uint64_t>(p.kv) +
-                             (uint64_t(uint32_t(blk) & uint32_t(mask)) * kBlock + (j0 % kBlock)) * kRowB;
-        const uint64_t src = (row & mask) | (reinterpret_cast<uint64_t>(kZeroRow) & ~mask);
         bad_slot[slot] = bad;
-        return Src{reinterpret_cast<const uint8_t*>(src), max(min(v, kSub) - 1, 0) & int(uint32_t(mask))};
+        return SrcA{j0, v, 0ull - uint64_t(v > 0 && !bad)};
+    };
+    auto source_b = [&](const SrcA& a, int32_t blk) -> uint64_t {
+        return reinterpret_cast<uint64_t>(p.kv) +
+               (uint64_t(uint32_t(blk) & uint32_t(a.mask)) * kBlock + (a.j0 % kBlock)) * kRowB;
+    };
+    auto source_c = [&](const SrcA& a, uint64_t row) -> Src {
+        const uint64_t src = (row & a.mask) | (reinterpret_cast<uint64_t>(kZeroRow) & ~a.mask);
+        return Src{reinterpret_cast<const uint8_t*>(src), max(min(a.v, kSub) - 1, 0) & int(uint32_t(a.mask))};
+    };
+    auto source = [&](int j, int32_t blk, auto slot_c) -> Src {
+        const SrcA a = source_a(j, blk, slot_c);
+        return source_c(a, source_b(a, blk));
     };
     // load k of this wave for a sub-tile in `slot`: k < 8 the latent part of
     // row 4k + w, k = 8 the rope parts of rows 8w .. 8w + 7.  Branch free:
@@ -234,7 +248,10 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         issue(1, S1{});
         issue(2, S2{});
     }
-    int32_t blk_ahead = block_of(kAhead);  // block id of the next sub-tile to load
+    // load source of the next iteration's sub-tile (j + kAhead + 1), formed one
+    // iteration ahead, and the block id of the one after it
+    Src ld_next = source(kAhead, block_of(kAhead), std::integral_constant<int, kAhead % kRing>{});
+    int32_t blk_ahead = block_of(kAhead + 1);
 
     f32x16 acc[kDvT];
 #pragma unroll
@@ -384,7 +401,16 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         // row into that free slot (no sub-tile uses it again), so the issue
         // path has no branch.
         using SL = std::integral_constant<int, (sc + kAhead) % kRing>;
-        const Src ld = source(j + kAhead, blk_ahead, SL{});
+        // ld was formed in the last iteration.  The source of the next
+        // iteration's sub-tile (j + kAhead + 1, into this iteration's slot sc)
+        // is formed here in three stages at light score-step slots of the last
+        // phase; the block id's scalar load (issued at the end of the last
+        // iteration) is waited for at slot 0, together with the first K reads,
+        // so that no later wait drains the LDS reads in flight.
+        const Src ld = ld_next;
+        const int32_t blk = blk_ahead;
+        SrcA ld_a;
+        uint64_t ld_row = 0;
         // a bad block id's sub-tile holds zero rows: all its scores are
         // masked below; no early exit
         const int cnt = bad_slot[sc] ? 0 : sub_count(j);
@@ -476,6 +502,21 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
                 }
             });
             if constexpr (s == kSumSlot) l += xhalf_sum(ps0 + ps1);
+            if constexpr (s == 0) asm volatile("" ::"s"(blk));
+            // (each stage's results are pinned to its slot by an empty asm use:
+            // the compiler would otherwise sink the chain next to the loads)
+            if constexpr (s == kC0 + 2) {
+                ld_a = source_a(j + kAhead + 1, blk, slot_c);
+                asm volatile("" ::"s"(ld_a.j0), "s"(ld_a.v), "s"(ld_a.mask));
+            }
+            if constexpr (s == kC0 + 5) {
+                ld_row = source_b(ld_a, blk);
+                asm volatile("" ::"s"(ld_row));
+            }
+            if constexpr (s == kC0 + 8) {
+                ld_next = source_c(ld_a, ld_row);
+                asm volatile("" ::"s"(ld_next.src), "s"(ld_next.last));
+            }
             // the first two V^T fragments, two slots before the first output MFMA
             if constexpr (s == pv_slot(0) - 2) vf[0] = vread(sc, 0, 0);
             if constexpr (s == pv_slot(0) - 1) vf[1] = vread(sc, 0, 1);
@@ -497,7 +538,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         // Every LDS read of this iteration has been consumed: a scalar load
         // issued now is waited for only by the next iteration's source, after
         // its barrier.
-        blk_ahead = block_of(j + kAhead + 1);
+        blk_ahead = block_of(j + kAhead + 2);
         __builtin_amdgcn_sched_barrier(0);
         // wait states before the next iteration's VALU reads the scores just
         // accumulated (the compiler does not see the asm as an MFMA)
