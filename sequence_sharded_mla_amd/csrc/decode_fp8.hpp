@@ -298,7 +298,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         const int32_t j0 = tok0 + j * kSub;
         const int v = min(kSub, tok1 - j0);  // <= 0: padding
         if constexpr (SPARSE) {
-            return SrcF{kZeroRow, j0, (v > 0 ? v : 1) - 1, v};
+            return SrcF{v > 0 ? p.kv : kZeroRow, j0, (v > 0 ? v : 1) - 1, v};
         } else {
             const bool bad = v > 0 && uint32_t(blk) >= pool32;
             const bool use = v > 0 && !bad;
@@ -310,6 +310,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
             return SrcF{reinterpret_cast<const uint8_t*>(src), j0, max(v - 1, 0) & int(uint32_t(mask)), v};
         }
     };
+    int32_t grow[SPARSE ? kLoads : 1];  // sparse: pool rows of the next sub-tile's loads
     // Load kk of this wave for the sub-tile of r in `slot`: kk < kCodeLoads a
     // code load, then kRopeLoads rope loads, then the scale load.
     auto load_one = [&](const SrcF& r, auto slot_c, auto kk_c) {
@@ -336,27 +337,44 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
                 if (lane < kSclRows) dma16_at<slot * kSclB>(r.src, min(s_row, r.last) * kRowF + kScaleOff, ls0);
             }
         } else {
-            // gathered rows: each lane addresses its own row of the list
-            auto rowp = [&](int t) -> const uint8_t* {
-                if (r.v <= 0) return kZeroRow;
-                return p.kv + int64_t(sm.rows[r.j0 + (t < r.last ? t : r.last)]) * kRowF;
-            };
+            // gathered rows: each lane addresses its own row of the list,
+            // whose pool row was read from LDS ahead of time (grow[kk], 0
+            // when the sub-tile is padding, with r.src the zero row)
+            const uint8_t* rowp = r.src + int64_t(grow[kk]) * kRowF;
             if constexpr (kk < kCodeLoads) {
                 constexpr int k = kk;
-                const int t = 2 * (wv * kCodeLoads + k) + h;
-                dma16_v_at<slot * kCodesB + k * 1024>(rowp(t) + (c_x ^ (u_bits(k) << 4)), lc0);
+                dma16_v_at<slot * kCodesB + k * 1024>(rowp + (c_x ^ (u_bits(k) << 4)), lc0);
             } else if constexpr (kk < kCodeLoads + kRopeLoads) {
                 constexpr int k = kk - kCodeLoads;
-                const int t = 8 * (wv * kRopeLoads + k) + rr;
-                dma16_v_at<slot * kRopeSB + k * 1024>(rowp(t) + (r_x ^ ((4 * (k & 1)) << 4)) + kRopeOff, lr0);
+                dma16_v_at<slot * kRopeSB + k * 1024>(rowp + (r_x ^ ((4 * (k & 1)) << 4)) + kRopeOff, lr0);
             } else {
-                if (lane < kSclRows) dma16_v_at<slot * kSclB>(rowp(s_row) + kScaleOff, ls0);
+                if (lane < kSclRows) dma16_v_at<slot * kSclB>(rowp + kScaleOff, ls0);
             }
+        }
+    };
+    // Sparse: the pool row behind each of this lane's loads of sub-tile r
+    // (the list entry of its token, rows past r.last re-reading r.last), read
+    // from LDS in one batch well before the loads are issued, so that no load
+    // waits for an LDS read (a wait that would also drain the operand reads
+    // in flight).  Padding sub-tiles read entry 0 and use the zero row.
+    auto gather_rows = [&](const SrcF& r) {
+        if constexpr (SPARSE) {
+            const int vmask = r.v > 0 ? -1 : 0;
+            static_for<0, kLoads>([&](auto kc) {
+                constexpr int kk = decltype(kc)::value;
+                int t;
+                if constexpr (kk < kCodeLoads) t = 2 * (wv * kCodeLoads + kk) + h;
+                else if constexpr (kk < kCodeLoads + kRopeLoads) t = 8 * (wv * kRopeLoads + kk - kCodeLoads) + rr;
+                else t = min(s_row0, kSub - 1);
+                const int e = (r.j0 + min(t, r.last)) & vmask;
+                grow[kk] = sm.rows[e] & vmask;
+            });
         }
     };
     // all loads of sub-tile j at once (the two sub-tiles before the loop)
     auto issue = [&](int j, auto slot_c) {
         const SrcF r = prep(j, block_of(j), slot_c);
+        gather_rows(r);
         static_for<0, kLoads>([&](auto kc) { load_one(r, slot_c, kc); });
     };
     // real rows of sub-tile j (0 for padding); its scores past that are masked
@@ -418,7 +436,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         // zero row into that free slot (no sub-tile reads it again), so the
         // issue path has no branch.
         using SL = std::integral_constant<int, (sc + 2) % kRingF>;
-        const bool do_load = !SPARSE || j + 2 < n_pad;
+        // (sparse: past the last sub-tile the loads read the zero row into
+        // the free slot, as dense ones do)
         const SrcF ld = (!SPARSE || j + 2 < n_pad) ? prep(j + 2, blk_ahead, SL{}) : SrcF{kZeroRow, 0, 0, 0};
         const int cnt = bad_slot[sc] ? 0 : sub_count(j);
         bad_block |= bad_slot[sc];
@@ -504,15 +523,20 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
 #pragma unroll
             for (int c = 0; c < 4; ++c) scr[c] = sread(0, c);
         }
+        // sparse: pool rows of sub-tile j+2's loads, read under the softmax
+        gather_rows(ld);
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- online softmax (log2 domain, lagging reference max) ----------
         if (__builtin_expect(cnt < kSub, 0)) {
+            // st[i] holds token (i >> 2) * 8 + 4 half + (i & 3): compared as
+            // a constant against cnt - 4 half, formed here (hoisted per-lane
+            // token numbers would be spilled out of the full register file)
+            int lim = cnt - 4 * half;
+            asm volatile("" : "+v"(lim));
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int tok = (i >> 2) * 8 + half * 4 + (i & 3);
-                if (tok >= cnt) st[i] = -INFINITY;
-            }
+            for (int i = 0; i < 16; ++i)
+                if ((i >> 2) * 8 + (i & 3) >= lim) st[i] = -INFINITY;
         }
         float mt3[5];
 #pragma unroll
@@ -574,11 +598,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
             if constexpr (g < 3 && e < 4) scr[e] = sread(g + 1, e);
             if constexpr (g < 3 && e >= 4) pscale(g + 1, e - 4, scr[e - 4]);
             if constexpr (u % 3 == 1 && u / 3 < kLoads) {
-                if (SPARSE) {
-                    if (do_load) load_one(ld, SL{}, std::integral_constant<int, u / 3>{});
-                } else {
-                    load_one(ld, SL{}, std::integral_constant<int, u / 3>{});
-                }
+                load_one(ld, SL{}, std::integral_constant<int, u / 3>{});
             }
             __builtin_amdgcn_sched_barrier(0);
         });
