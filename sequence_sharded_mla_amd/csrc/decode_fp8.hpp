@@ -316,25 +316,31 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     auto load_one = [&](const SrcF& r, auto slot_c, auto kk_c) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr int kk = decltype(kk_c)::value;
-        // opaque copies: the per-load offsets below are then computed here,
-        // not hoisted out of the loop into a dozen live registers
-        int c_x = c_x0, r_x = r_x0, s_row = s_row0;
-        asm volatile("" : "+v"(c_x), "+v"(r_x), "+v"(s_row));
+        // an opaque copy of the one base this load uses: its offset is then
+        // computed here, not hoisted out of the loop into a dozen live
+        // registers.  Row offsets are 24-bit products (t < 32, 656-byte rows).
+        auto opaque = [](int x) {
+            asm volatile("" : "+v"(x));
+            return x;
+        };
         if constexpr (!SPARSE) {
             // branch free: rows past r.last re-read row r.last (one v_min per
             // load; a whole sub-tile has r.last = 31 and clamps nothing)
             if constexpr (kk < kCodeLoads) {
                 constexpr int k = kk;
                 const int t = 2 * (wv * kCodeLoads + k) + h;
-                dma16_at<slot * kCodesB + k * 1024>(r.src, (c_x ^ (u_bits(k) << 4)) + min(t, r.last) * kRowF,
-                                                    lc0);
+                dma16_at<slot * kCodesB + k * 1024>(
+                    r.src, (opaque(c_x0) ^ (u_bits(k) << 4)) + int(__umul24(min(t, r.last), kRowF)), lc0);
             } else if constexpr (kk < kCodeLoads + kRopeLoads) {
                 constexpr int k = kk - kCodeLoads;
                 const int t = 8 * (wv * kRopeLoads + k) + rr;
                 dma16_at<slot * kRopeSB + k * 1024>(
-                    r.src, (r_x ^ ((4 * (k & 1)) << 4)) + kRopeOff + min(t, r.last) * kRowF, lr0);
+                    r.src, (opaque(r_x0) ^ ((4 * (k & 1)) << 4)) + kRopeOff + int(__umul24(min(t, r.last), kRowF)),
+                    lr0);
             } else {
-                if (lane < kSclRows) dma16_at<slot * kSclB>(r.src, min(s_row, r.last) * kRowF + kScaleOff, ls0);
+                if (lane < kSclRows)
+                    dma16_at<slot * kSclB>(r.src, int(__umul24(min(opaque(s_row0), r.last), kRowF)) + kScaleOff,
+                                           ls0);
             }
         } else {
             // gathered rows: each lane addresses its own row of the list,
@@ -343,10 +349,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
             const uint8_t* rowp = r.src + int64_t(grow[kk]) * kRowF;
             if constexpr (kk < kCodeLoads) {
                 constexpr int k = kk;
-                dma16_v_at<slot * kCodesB + k * 1024>(rowp + (c_x ^ (u_bits(k) << 4)), lc0);
+                dma16_v_at<slot * kCodesB + k * 1024>(rowp + (opaque(c_x0) ^ (u_bits(k) << 4)), lc0);
             } else if constexpr (kk < kCodeLoads + kRopeLoads) {
                 constexpr int k = kk - kCodeLoads;
-                dma16_v_at<slot * kRopeSB + k * 1024>(rowp + (r_x ^ ((4 * (k & 1)) << 4)) + kRopeOff, lr0);
+                dma16_v_at<slot * kRopeSB + k * 1024>(rowp + (opaque(r_x0) ^ ((4 * (k & 1)) << 4)) + kRopeOff, lr0);
             } else {
                 if (lane < kSclRows) dma16_v_at<slot * kSclB>(rowp + kScaleOff, ls0);
             }
