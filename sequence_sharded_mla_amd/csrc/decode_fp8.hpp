@@ -74,7 +74,7 @@ struct alignas(16) SmemFp8 {
     // barriers after its last read, so the shared copy needs no extra sync.
     float sct[kRingF][4][kSub];
     uint8_t qrope[NW * 32 * kRope * 2];   // [head][8 chunks], chunk c at c ^ ((head >> 1) & 7)
-    int32_t rows[SPARSE ? kMaxTopk : 1];  // sparse: pool rows this shard owns, entry order
+    int32_t rows[SPARSE ? kMaxTopk + 1 : 1];  // sparse: pool rows this shard owns, entry order; a spare slot
     int32_t wave_cnt[NW];
 };
 
@@ -115,20 +115,22 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
     if (visible < 0) visible = 0;
 
     // ---- query fragments: latent in registers (paired-step order), rope
-    // part through LDS.  Issued first, so that their latency overlaps the
-    // sparse compaction's loads.
+    // part through LDS.  A dense row requests them first; a sparse row right
+    // after its index and block-table loads, so that the compaction waits
+    // for those alone while the query is still in flight.
     bf16x8 qf[kQLatSteps];
     bf16x8 qrope_r[4];
     const int qr_off = head * (kRope * 2);
     const int qr_sw = (head >> 1) & 7;
-    {
+    auto load_query = [&] {
         const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
             static_cast<const uint16_t*>(p.q) + (size_t(id.qi) * p.H + head) * kDk);
 #pragma unroll
         for (int ks = 0; ks < kQLatSteps; ++ks) qf[ks] = qrow[4 * (ks >> 1) + 2 * half + (ks & 1)];
 #pragma unroll
         for (int u = 0; u < 4; ++u) qrope_r[u] = qrow[2 * (kQLatSteps + u) + half];
-    }
+    };
+    if constexpr (!SPARSE) load_query();
 
     // ---- the tokens this workgroup attends ---------------------------------
     int32_t tok0 = 0, tok1 = 0;  // dense: local token range; sparse: list range
@@ -176,31 +178,59 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
             const int32_t e = e_begin + k * 64 + lane;
             gv[k] = e < e_end ? idx[e] : -1;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        load_query();
+        __builtin_amdgcn_sched_barrier(0);
         if (bt_lds) {
-            wait_vm<0>();  // this wave's table loads (and the query and index loads)
+            // a use of the last index makes the compiler wait for the index
+            // loads, and so for this wave's table loads issued before them,
+            // but not for the query loads issued after
+#pragma unroll
+            for (int k = 0; k < kSteps; ++k) asm volatile("" ::"v"(gv[k]));
             __syncthreads();
         }
+        // Branch free: every entry looks up a table entry (a clamped index
+        // when it is not owned or past the table), all lookups are issued
+        // before any is used, and each error bit is raised once per wave.
+        // row: pool row of an owned entry, -1 not owned (or padding, or past
+        // the visible prefix: MLA_DEVERR_INDEX), -2 owned with a bad or
+        // missing table entry (MLA_DEVERR_BLOCK_TABLE).
         const double inv_n = 1.0 / double(p.n_shards);
-        int32_t row[kSteps];
+        int32_t row[kSteps], jl[kSteps];
+        bool bad_index = false, bad_table = false;
 #pragma unroll
         for (int k = 0; k < kSteps; ++k) {
             const int32_t g = gv[k];
-            const int32_t j = div_by(g < 0 ? 0 : g, inv_n);  // local index if owned
-            row[k] = -1;
-            if (g >= visible) {
-                raise_error(p.err, MLA_DEVERR_INDEX);
-            } else if (g >= 0 && g - j * p.n_shards == s) {
-                // block id for now
-                row[k] = j / kBlock >= p.max_blocks ? -1 : bt_lds ? bt_l[j / kBlock] : bt[j / kBlock];
-                row[k] = row[k] >= 0 && row[k] < p.pool_blocks ? row[k] * kBlock + (j % kBlock) : -2;
-            }
+            const int32_t gc = g < 0 ? 0 : g;
+            const int32_t j = div_by(gc, inv_n);  // local index if owned
+            bad_index |= g >= visible;
+            const bool owned = g >= 0 && g < visible && gc - j * p.n_shards == s;
+            jl[k] = owned ? j : -1;
+            const int32_t jb = j / kBlock;
+            row[k] = jb < p.max_blocks ? jb : 0;  // table index for now
         }
+        if (bt_lds) {
+#pragma unroll
+            for (int k = 0; k < kSteps; ++k) row[k] = bt_l[row[k]];  // block id for now
+        } else {
+#pragma unroll
+            for (int k = 0; k < kSteps; ++k) row[k] = bt[row[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k) {
+            const int32_t j = jl[k], b = row[k];
+            const bool ok = j / kBlock < p.max_blocks && b >= 0 && b < p.pool_blocks;
+            row[k] = j < 0 ? -1 : ok ? b * kBlock + (j % kBlock) : -2;
+            bad_table |= row[k] == -2;
+        }
+        if (lane == 0 && __ballot(bad_index)) raise_error(p.err, MLA_DEVERR_INDEX);
+        if (lane == 0 && __ballot(bad_table)) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
         int cnt = 0;
 #pragma unroll
         for (int k = 0; k < kSteps; ++k) {
-            if (row[k] == -2) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
+            // entries not kept write the spare slot (no branch per entry)
             const uint64_t mask = __ballot(row[k] >= 0);
-            if (row[k] >= 0) sm.rows[e_begin + cnt + __popcll(mask & below)] = row[k];
+            sm.rows[row[k] >= 0 ? e_begin + cnt + __popcll(mask & below) : kMaxTopk] = row[k];
             cnt += __popcll(mask);
         }
         if (lane == 0) sm.wave_cnt[wave] = cnt;
@@ -214,19 +244,18 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_fp8_kernel(DecodeParam
         }
         // Move every wave's entries to their final position.  A later wave's
         // destination can overlap an earlier wave's source, so all waves
-        // read first, then all write.
-        constexpr int kPerLane = kMaxTopk / (NW * 64);  // slice <= kMaxTopk / NW
+        // read first, then all write.  Branch free: every read stays inside
+        // the list (e_begin + i < kMaxTopk, since slice <= kMaxTopk / NW),
+        // and lanes past the count write the spare slot.
+        constexpr int kPerLane = kMaxTopk / (NW * 64);
         int32_t mine[kPerLane];
 #pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            const int i = k * 64 + lane;
-            mine[k] = i < cnt ? sm.rows[e_begin + i] : 0;
-        }
+        for (int k = 0; k < kPerLane; ++k) mine[k] = sm.rows[e_begin + k * 64 + lane];
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
             const int i = k * 64 + lane;
-            if (i < cnt) sm.rows[base + i] = mine[k];
+            sm.rows[i < cnt ? base + i : kMaxTopk] = mine[k];
         }
         __syncthreads();
         tok1 = total_owned;
