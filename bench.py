@@ -31,6 +31,13 @@ METRIC = "MLA decode attention: achieved HBM GB/s (% of peak) and KV tokens/s at
 KERNEL_SOURCES = ["decode_valu.hpp", "decode_mfma.hpp", "decode_fp8.hpp", "mfma_common.hpp", "common.hpp",
                   "params.hpp", "api.hip",
                   "reduce.hpp", "plan.hpp", "host.cpp"]
+# the sources a decode step's kernels are compiled from, per cache dtype: the
+# kernel family of that dtype plus the shared helpers, plan, combine, merge
+# and launch code (each family's header includes no other family's)
+_DECODE_SHARED = ["mfma_common.hpp", "common.hpp", "params.hpp", "api.hip", "reduce.hpp", "plan.hpp", "host.cpp"]
+DECODE_SOURCES = {"bf16": ["decode_mfma.hpp"] + _DECODE_SHARED,
+                  "fp8_ds": ["decode_fp8.hpp"] + _DECODE_SHARED,
+                  "f32": ["decode_valu.hpp"] + _DECODE_SHARED}
 WRITE_SOURCES = ["kv_write.hpp", "common.hpp", "api.hip"]
 TOPK_SOURCES = ["topk.hpp", "common.hpp", "api.hip"]
 TOPK_METRIC = "DCP top-K index selection: achieved HBM GB/s (% of peak) and rows/s, per-shard top-2048 + merge"
@@ -525,7 +532,7 @@ def run_varlen(args):
     part_ms = float(np.mean(t_part))
     achieved = launch_bytes / (part_ms * 1e-3) / 1e9
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    khash = kernel_hash()
+    khash = kernel_hash(DECODE_SOURCES[sp.kv_dtype])
     rec = {
         "metric": VARLEN_METRIC,
         "value": round(gbs, 2),
@@ -739,7 +746,7 @@ def main():
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     part_ms = float(np.mean(t_part))
     achieved = launch_bytes / (part_ms * 1e-3) / 1e9
-    khash = kernel_hash()
+    khash = kernel_hash(DECODE_SOURCES[sp.kv_dtype])
     prof = profile_record(sp.name, khash)
     stream_med = stream_best = None
     if extras:
