@@ -173,6 +173,29 @@ def test_sparse_repeated_positions(kv, heads):
     compare(x, step)
 
 
+@pytest.mark.parametrize("heads,n_shards", [(64, 1), (128, 1), (64, 2), (128, 2)])
+def test_sparse_full_list_one_owner(heads, n_shards):
+    """The longest top-K list the matrix-core sparse kernel keeps in LDS
+    (2048 entries), every entry owned by the last shard: each wave keeps its
+    whole slice, and with two shards the first shard's workgroup drops every
+    entry (an empty row, (0, -inf))."""
+    N = n_shards
+    ctx = 2048 * N + 300
+    sp = S["sparse_fp8_topk2048"].with_(batch=1, context=ctx, topk=2048, heads=heads, n_shards=N,
+                                        seed=31 + heads + N)
+    x = workload.generate(sp)
+    rng = np.random.default_rng(77)
+    for t in range(sp.q_len):
+        vis = ctx - sp.q_len + t + 1
+        x.topk_idx[0, t] = rng.permutation(np.arange(N - 1, vis, N))[:2048]
+    x = _reselect(x)
+    say(f"sparse full list, one owner: H={heads} N={N}")
+    _, step = run_gpu(x)
+    compare(x, step)
+    if N == 2:
+        assert np.all(np.isneginf(to_np(step.lses).reshape(N, 1, sp.q_len, heads)[0]))
+
+
 def _reselect(x):
     """Regenerate stored rows after editing topk_idx (materialise the union)."""
     sp = x.spec
