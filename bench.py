@@ -35,7 +35,7 @@ KERNEL_SOURCES = ["decode_valu.hpp", "decode_mfma.hpp", "decode_fp8.hpp", "mfma_
 # kernel family of that dtype plus the shared helpers, plan, combine, merge
 # and launch code (each family's header includes no other family's)
 _DECODE_SHARED = ["mfma_common.hpp", "common.hpp", "params.hpp", "api.hip", "reduce.hpp", "plan.hpp", "host.cpp"]
-DECODE_SOURCES = {"bf16": ["decode_mfma.hpp"] + _DECODE_SHARED,
+DECODE_SOURCES = {"bf16": ["decode_mfma.hpp", "sparse_list.hpp"] + _DECODE_SHARED,
                   "fp8_ds": ["decode_fp8.hpp"] + _DECODE_SHARED,
                   "f32": ["decode_valu.hpp"] + _DECODE_SHARED}
 WRITE_SOURCES = ["kv_write.hpp", "common.hpp", "api.hip"]

@@ -60,6 +60,10 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     uint8_t* w = static_cast<uint8_t*>(ws);
     p.err = err_word ? err_word : reinterpret_cast<uint32_t*>(w);
     p.plan_hdr = reinterpret_cast<const int32_t*>(w);
+    if (plan.sp_list) {
+        p.sp_list = reinterpret_cast<const int32_t*>(w + plan.sp_list_off);
+        p.sp_count = reinterpret_cast<const int32_t*>(w + plan.sp_count_off);
+    }
     if (plan.planned) {
         p.items = reinterpret_cast<const int32_t*>(w + plan.items_off);
         p.row_info = reinterpret_cast<const int32_t*>(w + plan.row_info_off);
@@ -99,11 +103,23 @@ int32_t decode_impl(const mla_decode_desc* d, const void* q, const void* kv_pool
     const uint32_t n_items = uint32_t(plan.items_max);
     // bf16 dense: every supported head count (16 pads to 32); 128 / H' output
     // dimension parts per head group keep all four waves busy
-    const bool mfma_bf16 = d->kv_dtype == MLA_BF16 && d->topk == 0 &&
+    // bf16 top-K: when the workspace holds the list pass's output
+    const bool mfma_bf16 = d->kv_dtype == MLA_BF16 && (d->topk == 0 || plan.sp_list) &&
                            (d->num_heads == 16 || d->num_heads == 32 || d->num_heads == 64 || d->num_heads == 128);
     const bool mfma_fp8 = d->kv_dtype == MLA_FP8_DS && (d->num_heads == 64 || d->num_heads == 128) &&
                           d->topk <= mfma::kMaxTopk;
-    if (mfma_bf16) {
+    if (mfma_bf16 && d->topk > 0) {
+        hipLaunchKernelGGL(sparse_list_kernel, dim3(uint32_t(plan.rows)), dim3(kListThreads), 0, s, p,
+                           reinterpret_cast<int32_t*>(w + plan.sp_list_off),
+                           reinterpret_cast<int32_t*>(w + plan.sp_count_off));
+        if ((st = launch_status()) != MLA_OK) return st;
+        if (d->num_heads == 128)
+            hipLaunchKernelGGL((mfma::decode_mfma_bf16_kernel<1, true>), dim3(n_items), dim3(256), 0, s, p);
+        else if (d->num_heads == 64)
+            hipLaunchKernelGGL((mfma::decode_mfma_bf16_kernel<2, true>), dim3(n_items), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((mfma::decode_mfma_bf16_kernel<4, true>), dim3(n_items), dim3(256), 0, s, p);
+    } else if (mfma_bf16) {
         if (d->num_heads == 128)
             hipLaunchKernelGGL(mfma::decode_mfma_bf16_kernel<1>, dim3(n_items), dim3(256), 0, s, p);
         else if (d->num_heads == 64)

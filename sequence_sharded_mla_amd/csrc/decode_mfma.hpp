@@ -36,6 +36,7 @@
 #include "common.hpp"
 #include "mfma_common.hpp"
 #include "params.hpp"
+#include "sparse_list.hpp"
 
 namespace mla {
 namespace mfma {
@@ -76,7 +77,13 @@ struct alignas(16) SmemBf16 {
     uint8_t qrope[kQRopeB];  // [head][8 chunks of 16 B], chunk c at c ^ ((head >> 1) & 7)
 };
 
-template <int DS>
+// SPARSE: a top-K step.  The row's tokens are the pool rows a list pass
+// (sparse_list.hpp) wrote for it, in entry order, and each wave gathers rows
+// 8w .. 8w + 7 of a sub-tile: one direct load per row for the latent parts
+// (its row address read from the list through the scalar cache), and one
+// load for their rope parts with a per-lane address.  Everything after the
+// loads is the dense path's.
+template <int DS, bool SPARSE = false>
 __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p) {
     static_assert(DS == 1 || DS == 2 || DS == 4, "output dimension splits");
     constexpr int kHG = 4 / DS;             // head groups of 32
@@ -94,18 +101,23 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     const int s = p.shard_begin + id.s_rel;
     const int32_t* bt = p.block_tables + (size_t(id.s_rel) * p.B + id.b) * p.max_blocks;
 
-    // ---- token range of this chunk ---------------------------------------
-    const int32_t L = p.context_lens[id.b];
-    int32_t visible = L - id.qlen + id.t + 1;
-    if (visible < 0) visible = 0;
-    int32_t local = dev_local_len(visible, s, p.n_shards);
-    if ((local + kBlock - 1) / kBlock > p.max_blocks) {
-        if (threadIdx.x == 0) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
-        local = p.max_blocks * kBlock;
+    // ---- token range of this chunk (sparse: of the row's list) ------------
+    int32_t tok0 = 0, tok1 = 0;
+    if constexpr (!SPARSE) {
+        const int32_t L = p.context_lens[id.b];
+        int32_t visible = L - id.qlen + id.t + 1;
+        if (visible < 0) visible = 0;
+        int32_t local = dev_local_len(visible, s, p.n_shards);
+        if ((local + kBlock - 1) / kBlock > p.max_blocks) {
+            if (threadIdx.x == 0) raise_error(p.err, MLA_DEVERR_BLOCK_TABLE);
+            local = p.max_blocks * kBlock;
+        }
+        tok0 = id.chunk * id.chunk_tok;
+        tok1 = id.chunk_tok ? tok0 + id.chunk_tok : local;
+        if (tok1 > local) tok1 = local;
+    } else {
+        tok1 = ((const __attribute__((address_space(4))) int32_t*)p.sp_count)[id.row];
     }
-    const int32_t tok0 = id.chunk * id.chunk_tok;
-    int32_t tok1 = id.chunk_tok ? tok0 + id.chunk_tok : local;
-    if (tok1 > local) tok1 = local;
     const int n_sub = tok1 > tok0 ? (tok1 - tok0 + kSub - 1) / kSub : 0;
     // the pipelined loop below is unrolled by the ring size and always runs
     // whole rounds: padding sub-tiles are zero rows with every score masked
@@ -143,15 +155,23 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     int dv[kSub / 4];  // latent loads of a full sub-tile
 #pragma unroll
     for (int k = 0; k < kSub / 4; ++k) {
-        const int t = 4 * k + wave;
-        dv[k] = t * kRowB + ((((lane & 48) | ((lane & 15) ^ swz(t)))) << 4);
+        if constexpr (!SPARSE) {
+            const int t = 4 * k + wave;
+            dv[k] = t * kRowB + ((((lane & 48) | ((lane & 15) ^ swz(t)))) << 4);
+        } else {
+            // sparse: load k of wave w is row 8w + k, from its own row address
+            const int t = 8 * wave + k;
+            dv[k] = (((lane & 48) | ((lane & 15) ^ swz(t)))) << 4;
+        }
     }
     const int r_row = 8 * wave + (lane >> 3);  // rope load: row and chunk of this lane
     const int r_off = (kLatent / 8 + ((lane & 7) ^ rswz(r_row))) << 4;
     // LDS destinations: lat_row(slot, 4k + w) = w * 8 KB + (k & 3) * 32 KB +
     // (k >> 2) * 1 KB + slot * 2 KB; rope_row(slot, 8w) = rope base + slot * 4 KB + w * 1 KB
     const uint32_t lds0 = lds_addr(sm.ring);
-    const uint32_t m_lat = __builtin_amdgcn_readfirstlane(lds0 + wv * (4 * 2 * kLatB));
+    // sparse: lat_row(slot, 8w + k) = (w & 1) * 64 KB + k * 8 KB + slot * 2 KB + (w >> 1) * 1 KB
+    const uint32_t m_lat = __builtin_amdgcn_readfirstlane(
+        SPARSE ? lds0 + (wv & 1) * (16 * 4 * kLatB) + (wv >> 1) * kLatB : lds0 + wv * (4 * 2 * kLatB));
     const uint32_t m_rope = __builtin_amdgcn_readfirstlane(lds0 + kLatRegion + wv * 8 * kRopeB);
 
     // Block ids are read through the scalar cache (the table is read-only
@@ -208,6 +228,63 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         const SrcA a = source_a(j, blk, slot_c);
         return source_c(a, source_b(a, blk));
     };
+    // Sparse: the list entries of sub-tile j this wave gathers (rows 8w ..
+    // 8w + 7 of the sub-tile), eight 32-bit pool rows read through the scalar
+    // cache in one load; a sub-tile past the last reads the list's first
+    // (inside the row; its values are unused).
+    const int64_t sp_stride = sparse_list_stride(p.topk);
+    auto list_of = [&](int j) -> i32x8 {
+        if constexpr (!SPARSE) {
+            return i32x8{};
+        } else {
+            const int jj = j < n_sub ? j : 0;
+            return *(const __attribute__((address_space(4))) i32x8*)(p.sp_list + size_t(id.row) * sp_stride +
+                                                                      jj * kSub + 8 * wv);
+        }
+    };
+    // Source of a sparse sub-tile: the row address of each of the wave's eight
+    // latent loads (the zero row for an entry past the list or a sub-tile past
+    // the last), and each lane's address for the rope load (row 8w + lane / 8,
+    // its chunk).  Formed in two stages (scalar bases, then the per-lane rope
+    // address) so that the main loop can deal them out over MFMA slots.
+    struct SrcSp {
+        uint64_t base[8];
+        uint64_t rope;
+    };
+    auto sp_bases = [&](int j, const i32x8& r, SrcSp& d) {
+        const bool in = j < n_sub;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            d.base[k] = in && r[k] >= 0 ? reinterpret_cast<uint64_t>(p.kv) + uint64_t(uint32_t(r[k])) * kRowB
+                                        : reinterpret_cast<uint64_t>(kZeroRow);
+    };
+    auto sp_rope = [&](int j, const i32x8& r, SrcSp& d) {
+        int32_t rl = r[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) rl = (lane >> 3) == k ? r[k] : rl;
+        const bool ok = j < n_sub && rl >= 0;
+        d.rope = (ok ? reinterpret_cast<uint64_t>(p.kv) + uint64_t(uint32_t(rl)) * kRowB
+                     : reinterpret_cast<uint64_t>(kZeroRow)) + uint32_t(r_off);
+    };
+    auto source_sp = [&](int j, const i32x8& r) -> SrcSp {
+        SrcSp d;
+        sp_bases(j, r, d);
+        sp_rope(j, r, d);
+        return d;
+    };
+    // sparse load k: k < 8 the latent part of row 8w + k, k = 8 the rope parts
+    // of rows 8w .. 8w + 7
+    auto load_sp = [&](const SrcSp& r, auto slot_c, auto k_c) {
+        constexpr int slot = decltype(slot_c)::value;
+        constexpr int k = decltype(k_c)::value;
+        if constexpr (k < kSub / 4) {
+            constexpr int imm = k * 8 * kLatB + slot * 2 * kLatB;
+            dma16_at<imm>(reinterpret_cast<const void*>(r.base[k]), dv[k], m_lat);
+        } else {
+            constexpr int imm = slot * kSub * kRopeB;
+            dma16_v_at<imm>(reinterpret_cast<const void*>(r.rope), m_rope);
+        }
+    };
     // load k of this wave for a sub-tile in `slot`: k < 8 the latent part of
     // row 4k + w, k = 8 the rope parts of rows 8w .. 8w + 7.  Branch free:
     // rows past r.last re-read row r.last through a row shift that is uniform
@@ -230,8 +307,13 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     // all loads of sub-tile j, issued together (one branch for the common
     // case of a whole valid sub-tile)
     auto issue = [&](int j, auto slot_c) {
-        const Src r = source(j, block_of(j), slot_c);
-        static_for<0, kLoadsPerWave>([&](auto kc) { load(r, slot_c, kc); });
+        if constexpr (SPARSE) {
+            const SrcSp r = source_sp(j, list_of(j));
+            static_for<0, kLoadsPerWave>([&](auto kc) { load_sp(r, slot_c, kc); });
+        } else {
+            const Src r = source(j, block_of(j), slot_c);
+            static_for<0, kLoadsPerWave>([&](auto kc) { load(r, slot_c, kc); });
+        }
     };
     // real rows of sub-tile j (0 for padding); its scores past that are masked
     auto sub_count = [&](int j) { return max(0, min(kSub, tok1 - tok0 - j * kSub)); };
@@ -250,8 +332,17 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
     }
     // load source of the next iteration's sub-tile (j + kAhead + 1), formed one
     // iteration ahead, and the block id of the one after it
-    Src ld_next = source(kAhead, block_of(kAhead), std::integral_constant<int, kAhead % kRing>{});
-    int32_t blk_ahead = block_of(kAhead + 1);
+    using LSrc = std::conditional_t<SPARSE, SrcSp, Src>;
+    using LAhead = std::conditional_t<SPARSE, i32x8, int32_t>;  // block id, or the list entries
+    LSrc ld_next;
+    LAhead blk_ahead;
+    if constexpr (SPARSE) {
+        ld_next = source_sp(kAhead, list_of(kAhead));
+        blk_ahead = list_of(kAhead + 1);
+    } else {
+        ld_next = source(kAhead, block_of(kAhead), std::integral_constant<int, kAhead % kRing>{});
+        blk_ahead = block_of(kAhead + 1);
+    }
 
     f32x16 acc[kDvT];
 #pragma unroll
@@ -407,8 +498,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         // phase; the block id's scalar load (issued at the end of the last
         // iteration) is waited for at slot 0, together with the first K reads,
         // so that no later wait drains the LDS reads in flight.
-        const Src ld = ld_next;
-        const int32_t blk = blk_ahead;
+        const LSrc ld = ld_next;
+        const LAhead blk = blk_ahead;
         SrcA ld_a;
         uint64_t ld_row = 0;
         // a bad block id's sub-tile holds zero rows: all its scores are
@@ -502,26 +593,46 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
                 }
             });
             if constexpr (s == kSumSlot) l += xhalf_sum(ps0 + ps1);
-            if constexpr (s == 0) asm volatile("" ::"s"(blk));
             // (each stage's results are pinned to its slot by an empty asm use:
             // the compiler would otherwise sink the chain next to the loads)
-            if constexpr (s == kC0 + 2) {
-                ld_a = source_a(j + kAhead + 1, blk, slot_c);
-                asm volatile("" ::"s"(ld_a.j0), "s"(ld_a.v), "s"(ld_a.mask));
-            }
-            if constexpr (s == kC0 + 5) {
-                ld_row = source_b(ld_a, blk);
-                asm volatile("" ::"s"(ld_row));
-            }
-            if constexpr (s == kC0 + 8) {
-                ld_next = source_c(ld_a, ld_row);
-                asm volatile("" ::"s"(ld_next.src), "s"(ld_next.last));
+            if constexpr (!SPARSE) {
+                if constexpr (s == 0) asm volatile("" ::"s"(blk));
+                if constexpr (s == kC0 + 2) {
+                    ld_a = source_a(j + kAhead + 1, blk, slot_c);
+                    asm volatile("" ::"s"(ld_a.j0), "s"(ld_a.v), "s"(ld_a.mask));
+                }
+                if constexpr (s == kC0 + 5) {
+                    ld_row = source_b(ld_a, blk);
+                    asm volatile("" ::"s"(ld_row));
+                }
+                if constexpr (s == kC0 + 8) {
+                    ld_next = source_c(ld_a, ld_row);
+                    asm volatile("" ::"s"(ld_next.src), "s"(ld_next.last));
+                }
+            } else {
+                if constexpr (s == 0)
+                    asm volatile("" ::"s"(blk[0]), "s"(blk[1]), "s"(blk[2]), "s"(blk[3]), "s"(blk[4]),
+                                 "s"(blk[5]), "s"(blk[6]), "s"(blk[7]));
+                if constexpr (s == kC0 + 2) {
+                    sp_bases(j + kAhead + 1, blk, ld_next);
+                    asm volatile("" ::"s"(ld_next.base[0]), "s"(ld_next.base[1]), "s"(ld_next.base[2]),
+                                 "s"(ld_next.base[3]));
+                    asm volatile("" ::"s"(ld_next.base[4]), "s"(ld_next.base[5]), "s"(ld_next.base[6]),
+                                 "s"(ld_next.base[7]));
+                }
+                if constexpr (s == kC0 + 8) {
+                    sp_rope(j + kAhead + 1, blk, ld_next);
+                    asm volatile("" ::"v"(ld_next.rope));
+                }
             }
             // the first two V^T fragments, two slots before the first output MFMA
             if constexpr (s == pv_slot(0) - 2) vf[0] = vread(sc, 0, 0);
             if constexpr (s == pv_slot(0) - 1) vf[1] = vread(sc, 0, 1);
             static_for<0, kLoadsPerWave>([&](auto kc) {
-                if constexpr (s == load_slot(decltype(kc)::value)) load(ld, SL{}, kc);
+                if constexpr (s == load_slot(decltype(kc)::value)) {
+                    if constexpr (SPARSE) load_sp(ld, SL{}, kc);
+                    else load(ld, SL{}, kc);
+                }
             });
             // the slot's MFMA
             static_for<0, kQSteps>([&](auto rc) {
@@ -538,7 +649,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_bf16_kernel(DecodeParams p
         // Every LDS read of this iteration has been consumed: a scalar load
         // issued now is waited for only by the next iteration's source, after
         // its barrier.
-        blk_ahead = block_of(j + kAhead + 2);
+        if constexpr (SPARSE) blk_ahead = list_of(j + kAhead + 2);
+        else blk_ahead = block_of(j + kAhead + 2);
         __builtin_amdgcn_sched_barrier(0);
         // wait states before the next iteration's VALU reads the scores just
         // accumulated (the compiler does not see the asm as an MFMA)

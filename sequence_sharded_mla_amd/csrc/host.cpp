@@ -111,6 +111,24 @@ int32_t make_plan(const mla_decode_desc* d, int32_t shard_count, Plan* plan, int
             while (p.target > 1 && planned_bytes(d, p, off) > ws_cap) p.target /= 2;
         off = size_planned(d, &p, off);
     }
+    // A top-K step on a bf16 cache runs on the matrix-core kernel behind a
+    // list pass whose output (each row's owned pool rows) lives in the
+    // workspace.  A capped workspace too small for the lists keeps the step
+    // on the VALU kernel, which needs none.
+    if (d->topk > 0 && d->kv_dtype == MLA_BF16) {
+        const int64_t stride = (int64_t(d->topk) + 31) / 32 * 32;
+        int64_t o2 = off;
+        const int64_t list_off = o2;
+        o2 = align_up(o2 + int64_t(p.rows) * stride * 4, 256);
+        const int64_t count_off = o2;
+        o2 = align_up(o2 + int64_t(p.rows) * 4, 256);
+        if (ws_cap <= 0 || o2 <= ws_cap) {
+            p.sp_list = true;
+            p.sp_list_off = list_off;
+            p.sp_count_off = count_off;
+            off = o2;
+        }
+    }
     p.ws_bytes = off;
     if (ws_cap > 0 && p.ws_bytes > ws_cap) return MLA_ERR_WORKSPACE;
     *plan = p;

@@ -23,6 +23,8 @@ struct DecodeParams {
     const int32_t* row_info;     // [rows][2] first partial slot (-1: none), items of the row
     const int32_t* plan_hdr;     // [0] error word, [1] item count, [2] tokens per chunk
     uint32_t* err;               // device error word
+    const int32_t* sp_list;      // bf16 top-K steps: [rows][stride] pool rows each shard owns, -1 after
+    const int32_t* sp_count;     // [rows] owned entries of each row
     int64_t pool_blocks;
     int32_t row_bytes;
     int32_t B, Tq, H, max_blocks, topk;

@@ -46,6 +46,9 @@ struct Plan {
     int64_t row_info_off = 0;   // int32 [rows][2]
     int64_t ws_o_off = 0;       // float [slots][H][512]
     int64_t ws_lse_off = 0;     // float [slots][H]
+    bool sp_list = false;       // top-K step on a bf16 cache: a list pass, then the matrix-core kernel
+    int64_t sp_list_off = 0;    // int32 [rows][topk rounded up to 32] pool rows each row owns
+    int64_t sp_count_off = 0;   // int32 [rows]
 };
 
 int64_t row_bytes(int32_t kv_dtype);

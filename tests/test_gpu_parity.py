@@ -208,7 +208,10 @@ def _reselect(x):
     offs = np.concatenate([[0], np.cumsum(counts)])
     T = int(offs[-1])
     lat = rng.standard_normal((T, 512), dtype=np.float32)
-    codes, scales = workload.quantize_fp8_groups(lat)
+    if sp.kv_dtype == "bf16":
+        codes, scales = workload._bf16_bits(lat), None
+    else:
+        codes, scales = workload.quantize_fp8_groups(lat)
     rope = workload._bf16_bits(rng.standard_normal((T, 64), dtype=np.float32))
     x.row_offsets, x.row_pos = offs, np.concatenate(pos_lists)
     x.latent, x.scales, x.rope = codes, scales, rope
@@ -442,3 +445,90 @@ def test_chunk_combine_more_than_64_chunks():
     rows = sp.batch * sp.q_len
     assert step.workspace.numel() > 64 * rows * sp.heads * 512 * 4, "expected > 64 chunks"
     compare(x, step)
+
+
+# ---- top-K steps over a bf16 cache: list pass + matrix-core kernel ---------
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+def test_bf16_sparse(heads):
+    sp = S["sparse_bf16_topk2048"].with_(batch=3, context=5000, topk=256, heads=heads, seed=40 + heads)
+    say(f"bf16 sparse H={heads}")
+    x = workload.generate(sp)
+    _, step = run_gpu(x)
+    compare(x, step)
+
+
+def test_bf16_sparse_empty_shards_padding_and_long_list():
+    """Every entry of one token on one shard, a token with no entry, padding
+    mid-list, and a list longer than the fp8 kernel keeps in LDS."""
+    sp = S["sparse_bf16_topk2048"].with_(batch=2, context=40000, topk=2500, heads=64, seed=50)
+    x = workload.generate(sp)
+    N = sp.n_shards
+    x.topk_idx[0, 0] = np.random.default_rng(5).permutation(np.arange(3, 39990, N))[:2500]
+    x.topk_idx[0, 1] = -1
+    x.topk_idx[1, 0, 100:] = -1
+    x = _reselect(x)
+    _, step = run_gpu(x)
+    compare(x, step)
+    lse = to_np(step.lses).reshape(N, 2, 2, sp.heads)
+    for s in range(N):
+        if s != 3:
+            assert np.all(np.isneginf(lse[s, 0, 0]))
+    assert np.all(np.isneginf(to_np(step.lse).reshape(2, 2, sp.heads)[0, 1]))
+
+
+@pytest.mark.parametrize("heads,n_shards", [(64, 1), (128, 2)])
+def test_bf16_sparse_full_list_one_owner(heads, n_shards):
+    N = n_shards
+    ctx = 2048 * N + 300
+    sp = S["sparse_bf16_topk2048"].with_(batch=1, context=ctx, topk=2048, heads=heads, n_shards=N,
+                                         seed=60 + heads + N)
+    x = workload.generate(sp)
+    rng = np.random.default_rng(78)
+    for t in range(sp.q_len):
+        vis = ctx - sp.q_len + t + 1
+        x.topk_idx[0, t] = rng.permutation(np.arange(N - 1, vis, N))[:2048]
+    x = _reselect(x)
+    _, step = run_gpu(x)
+    compare(x, step)
+
+
+def test_bf16_sparse_errors_and_single_shard_call():
+    """An entry past its token's prefix (MLA_DEVERR_INDEX) and a block id
+    outside the pool (MLA_DEVERR_BLOCK_TABLE): the offending entries are
+    dropped and every other result matches the oracle without them; one
+    shard's own call gives that shard's partials bit for bit."""
+    from sequence_sharded_mla_amd import MLA_DEVERR_BLOCK_TABLE, MLA_DEVERR_INDEX, alloc_workspace
+    sp = S["sparse_bf16_topk2048"].with_(batch=2, context=3000, topk=300, heads=64, seed=70)
+    x = workload.generate(sp)
+    N = sp.n_shards
+    cache = layout.pack(x, device="cuda")
+    idx = cache.topk_idx.clone()
+    idx[0, 0, 5] = 3000                # past the prefix of request 0's last token (2999 positions)
+    cache.topk_idx = idx
+    bt = cache.block_tables.clone()
+    bt[5, 1, 0] = cache.pool_blocks    # shard 5, request 1, local block 0
+    cache.block_tables = bt
+    step = ShardedDecodeStep(cache, sp.out_dtype)
+    step()
+    torch.cuda.synchronize()
+    err = mla_get_device_error(step.workspace)
+    assert err & MLA_DEVERR_INDEX and err & MLA_DEVERR_BLOCK_TABLE
+    mla_clear_device_error(step.workspace)
+    g = idx.cpu().numpy()
+    g[0, 0, 5] = -1
+    drop = (g[1] >= 0) & (g[1] % N == 5) & ((g[1] // N) // 64 == 0)
+    g[1][drop] = -1
+    assert drop.any()
+    x.topk_idx = g
+    compare(x, step)
+    d = cache.desc
+    ws = alloc_workspace(d, 1)
+    for s in (0, 5):
+        o = torch.empty_like(step.o_partials[s])
+        l = torch.empty_like(step.lses[s])
+        mla_decode_partial(d, cache.q, cache.pool, cache.block_tables[s].contiguous(), cache.context_lens,
+                           cache.topk_idx, s, N, o, l, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, step.o_partials[s]) and torch.equal(l, step.lses[s])

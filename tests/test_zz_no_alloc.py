@@ -49,6 +49,8 @@ def _both(sp, shard):
      ("dense_bf16_32k", dict(batch=1, context=700, heads=64, seed=44))),
     (("sparse_fp8_topk2048", dict(batch=3, context=6000, topk=512, seed=45)),
      ("sparse_fp8_topk2048", dict(batch=1, context=900, topk=128, seed=46))),
+    (("sparse_bf16_topk2048", dict(batch=3, context=6000, topk=512, seed=47)),
+     ("sparse_bf16_topk2048", dict(batch=1, context=900, topk=128, seed=48))),
 ])
 def test_noalloc_matches_workspace_call_twice(first, second):
     for name, kw in (first, second):

@@ -92,6 +92,12 @@ SPECS = {
                                 heads=64, n_shards=8, q_dtype="bf16",
                                 kv_dtype="fp8_ds", out_dtype="bf16",
                                 context=262144, topk=2048, seed=505),
+    # the same top-K step over a bf16 cache (a supported shape that runs on
+    # the VALU kernel; measured, not one of the headline workloads)
+    "sparse_bf16_topk2048": Spec("sparse_bf16_topk2048", batch=128, q_len=2,
+                                 heads=64, n_shards=8, q_dtype="bf16",
+                                 kv_dtype="bf16", out_dtype="bf16",
+                                 context=262144, topk=2048, seed=515),
 }
 
 
