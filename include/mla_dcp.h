@@ -135,6 +135,8 @@ int64_t mla_kv_row_bytes(int32_t kv_dtype);
  * word lives in the first 4 bytes).  Beyond the error word the workspace
  * holds the step's transient state: the chunk plan and the float32 partial
  * outputs of rows split into chunks (their combine is the LSE merge below),
+ * and, for a top-K step over a bf16 cache, each (shard, query token) row's
+ * list of the pool rows it owns (int32, the top-K width rounded up to 32),
  * bounded by desc alone, so a caller can reserve it once, apart from the
  * cache pool.  Keeping the attention workspace a known, separately measured
  * allocation is what "GLM-5.2 vLLM Decode Context Parallelism", section
