@@ -102,6 +102,15 @@ def test_fp8_sparse(heads):
     check(workload.generate(sp), [2, 1, 0, 2])
 
 
+@pytest.mark.parametrize("heads", [32, 128])
+def test_bf16_sparse(heads):
+    """Top-K over a bf16 cache with a query count per request: the list pass
+    resolves each row's request and position through the query map."""
+    sp = S["sparse_bf16_topk2048"].with_(batch=4, q_len=2, heads=heads, context=0,
+                                         ctx_range=(1500, 12000), topk=300, seed=75 + heads)
+    check(workload.generate(sp), [2, 1, 0, 2])
+
+
 def test_f32_vector_path():
     sp = S["tiny_f32"].with_(batch=4, q_len=3, context=0, ctx_range=(3, 300), seed=67)
     check(workload.generate(sp), [0, 3, 1, 2])
