@@ -92,6 +92,22 @@ def ws_size(lib, desc, shards=1):
     return st, out.value
 
 
+@pytest.mark.parametrize("topk,shards,q_len", [(1, 1, 1), (100, 8, 2), (2048, 3, 1), (2500, 8, 2)])
+def test_workspace_holds_the_bf16_topk_lists(lib, topk, shards, q_len):
+    """A top-K step over a bf16 cache needs, beyond what the same step over an
+    fp8 cache needs, each row's list of owned pool rows (int32, the top-K
+    width rounded up to 32) and its count, each region 256-byte aligned."""
+    def align(x):
+        return (x + 255) // 256 * 256
+    kw = dict(batch=5, q_len=q_len, topk=topk, max_blocks=64)
+    st8, n8 = ws_size(lib, good_desc(kv_dtype=_lib.MLA_FP8_DS, **kw), shards)
+    st16, n16 = ws_size(lib, good_desc(kv_dtype=_lib.MLA_BF16, **kw), shards)
+    assert st8 == 0 and st16 == 0
+    rows = shards * 5 * q_len
+    stride = (topk + 31) // 32 * 32
+    assert n16 - n8 == align(rows * stride * 4) + align(rows * 4)
+
+
 @pytest.mark.parametrize("field,value,code", [
     ("batch", -1, _lib.MLA_ERR_SHAPE),
     ("q_len", 0, _lib.MLA_ERR_SHAPE),
