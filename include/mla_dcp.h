@@ -174,7 +174,10 @@ int32_t mla_decode_partial(const mla_decode_desc* desc, const void* q, const voi
  *              mla_get_device_error(err_word, ...)), or NULL to drop them
  * A call whose chunk plan and partials would not fit in the scratch plans
  * fewer, longer chunks; if even that does not fit it returns
- * MLA_ERR_WORKSPACE (a call of more than about a million query tokens).
+ * MLA_ERR_WORKSPACE (a call of more than about a million query tokens).  A
+ * top-K step over a bf16 cache whose per-row lists would not fit (more than
+ * about 16 million list entries) runs on the slower vector kernel instead,
+ * with the same results.
  * Every call on one GPU shares that GPU's scratch: calls that overlap on one
  * GPU (different streams or threads without ordering between them) race and
  * give undefined results; calls ordered on one stream are fine. */
