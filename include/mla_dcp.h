@@ -176,8 +176,9 @@ int32_t mla_decode_partial(const mla_decode_desc* desc, const void* q, const voi
  * fewer, longer chunks; if even that does not fit it returns
  * MLA_ERR_WORKSPACE (a call of more than about a million query tokens).  A
  * top-K step over a bf16 cache whose per-row lists would not fit (more than
- * about 16 million list entries) runs on the slower vector kernel instead,
- * with the same results.
+ * about 16 million list entries) runs on the slower vector kernel instead
+ * (results within the same bounds against the definition, not bit for bit
+ * those of the workspace call).
  * Every call on one GPU shares that GPU's scratch: calls that overlap on one
  * GPU (different streams or threads without ordering between them) race and
  * give undefined results; calls ordered on one stream are fine. */
